@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module only draws and shapes random tensors and picks sample rows; it
+holds none of the attention arithmetic, so both the HIP path's tests and the
+CPU oracle can take their inputs from it without sharing any of the method.
+
+The workloads follow the shapes the pages measure on: the pages' Triton
+comparison runs [B, H, N, d] = [4, 32, 2048, 64] in fp16 ("Implementing
+FlashAttention 1 and 2 forward in Triton", section on the reference shape),
+and the CuTe write-up covers head dims 64 and 128 with sequences up to 64K
+("FlashAttention-2 from scratch in CuTe", summary).  No public dataset is
+involved: every tensor is i.i.d. Gaussian, drawn as float32 with numpy's
+PCG64 generator, scaled by sigma and rounded to fp16 (round-to-nearest-even).
+Draw order is Q, then K, then V from one generator seeded with ``seed``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_rows", "stress_inputs"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    sigma: float          # standard deviation of every Q, K, V element
+    seed: int = 0
+    sampled_rows: int = 0  # 0: every query row is checked; else rows per (b, h)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def flops(self) -> float:
+        """4*B*H*N^2*d (two GEMMs of 2*N^2*d each per head), halved if causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny", 1, 2, 256, 64, False, 1.0),
+        Workload("ref", 4, 32, 2048, 64, False, 1.0),
+        Workload("ref_causal", 4, 32, 2048, 64, True, 1.0),
+        Workload("ref_d128", 4, 32, 2048, 128, False, 1.0, sampled_rows=512),
+        Workload("hd128_16k", 2, 16, 16384, 128, False, 0.5, sampled_rows=512),
+        Workload("long_64k", 1, 16, 65536, 128, False, 0.5, sampled_rows=512),
+        Workload("long_64k_causal", 1, 16, 65536, 128, True, 0.5, sampled_rows=512),
+    ]
+}
+
+
+def make_qkv(B, H, N, d, sigma=1.0, seed=0):
+    """Q, K, V as fp16 numpy arrays [B, H, N, d], i.i.d. N(0, sigma^2)."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out.append(x.astype(np.float16))
+    return tuple(out)
+
+
+def sample_rows(N, b, h, count=512):
+    """Sorted query rows checked for (b, h): {0, N-1} plus count-2 distinct
+    rows drawn uniformly from [1, N-2] with generator seed [1000, b, h]."""
+    if N <= count:
+        return np.arange(N, dtype=np.int64)
+    rng = np.random.default_rng([1000, b, h])
+    mid = rng.choice(np.arange(1, N - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, N - 1], mid]).astype(np.int64))
+
+
+def stress_inputs(kind, B, H, N, d, seed=0):
+    """Structured fp16 inputs [B, H, N, d] that stress the recurrence.
+
+    rising   -- the score of key j grows with j, so the running max rises
+                on every key tile;
+    falling  -- the reverse: the first tile holds the row max;
+    large    -- Q, K ~ N(0, 4^2): scores far beyond exp's fp32 range;
+    const_v  -- every V row is the same vector;
+    zero_q   -- Q = 0: every score is 0, uniform weights.
+    """
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if kind in ("rising", "falling"):
+        ramp = np.linspace(-4.0, 4.0, N, dtype=np.float32)
+        if kind == "falling":
+            ramp = ramp[::-1].copy()
+        q *= np.float32(0.05)
+        q[..., 0] = 2.0
+        k *= np.float32(0.05)
+        k[..., 0] = ramp
+    elif kind == "large":
+        q *= np.float32(4.0)
+        k *= np.float32(4.0)
+    elif kind == "const_v":
+        v[:] = v[:, :, :1, :]
+    elif kind == "zero_q":
+        q[:] = 0.0
+    else:
+        raise ValueError(f"unknown stress input {kind!r}")
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
