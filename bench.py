@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the FlashAttention-2 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ref]
+
+A step is one fa2_fwd call: the whole hot path (load Q, stream K/V tiles,
+two MFMA contractions, online softmax, normalised O and LSE) over one batch
+of seeded synthetic fp16 inputs already resident in HBM.  Prints ONE JSON
+line on stdout; progress goes to stderr.
+
+value      TFLOP/s with FLOPs = 4*B*H*N^2*d (halved when causal), wall clock
+           over K steps between two device synchronisations;
+roofline   the kernel's average launch time from HIP events on the stream it
+           is launched on, against MI355X's dense fp16 MFMA peak;
+           ``traffic`` is the HBM bytes per launch measured by rocprofv3
+           counters for this exact kernel source (null if the source changed
+           since they were taken);
+cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded
+           sample of the same workload (a reported baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FA2 fwd TFLOP/s and % of MI355X fp16 MFMA peak, [4,32,2048,64]"
+PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_fwd_amd", "csrc", f)
+                  for f in ("fa2_fwd_gfx950.hip", "fa2_api.cpp", "fa2_launch.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256") != kernel_sha():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the oracle on whole (b, h) heads, as many as fit ~budget_s."""
+    import numpy as np
+
+    from exact_attention_fwd_amd.workloads import sample_rows
+    from oracle import attention_fp64
+    from oracle.attention import oracle_threads
+
+    threads = oracle_threads()
+    per_row_flops = 4.0 * w.N * w.d / (2 if w.causal else 1)
+    if w.sampled_rows:
+        rows = np.stack([np.stack([sample_rows(w.N, b, h, w.sampled_rows) for h in range(w.H)])
+                         for b in range(w.B)])
+        t0 = time.perf_counter()
+        attention_fp64(q, k, v, w.scale, causal=w.causal, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        flops = rows.size * per_row_flops
+        sample = f"{w.sampled_rows} seeded query rows per (b,h) of {w.name}, all {w.B * w.H} heads"
+    else:
+        # whole heads, the first n of them; n sized from a one-head probe
+        t0 = time.perf_counter()
+        attention_fp64(q[:1, :1], k[:1, :1], v[:1, :1], w.scale, causal=w.causal, threads=1)
+        one = max(time.perf_counter() - t0, 1e-4)
+        n_heads = int(min(w.B * w.H, max(threads, budget_s * threads / one)))
+        n_heads = max(1, n_heads)
+        qf, kf, vf = (x.reshape(1, w.B * w.H, w.N, w.d)[:, :n_heads] for x in (q, k, v))
+        t0 = time.perf_counter()
+        attention_fp64(qf, kf, vf, w.scale, causal=w.causal, threads=threads)
+        dt = time.perf_counter() - t0
+        flops = n_heads * w.N * per_row_flops
+        sample = f"{n_heads} of {w.B * w.H} heads of {w.name}, every query row"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ref")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the attention forward of one "
+              "(batch, head) shard needs no communication, so more GPUs would only shard B*H.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_fwd_amd as fa2
+    from exact_attention_fwd_amd.workloads import WORKLOADS, make_qkv, sample_rows
+
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa2.fwd(tq, tk, tv, scale=w.scale, causal=w.causal, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # HIP events on the stream the kernel is launched on (torch's current one).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flops = w.flops()
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: wall {ms_per_step:.4f} ms/step, events {ev_ms:.4f} ms/launch, "
+        f"{value:.1f} TFLOP/s ({100 * value / PEAK_FP16_TFLOPS:.1f}% of peak)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} [B={w.B},H={w.H},N={w.N},d={w.d}] "
+                               f"{'causal' if w.causal else 'non-causal'} fp16, N(0,{w.sigma:g}^2) inputs",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name),
+                     "launch_ms": round(ev_ms, 5)},
+    }
+
+    if not args.no_parity:
+        # sampled parity of the timed output, 64 seeded rows per (b, h)
+        from oracle import attention_fp64
+        rows = np.stack([np.stack([sample_rows(w.N, b, h, 64) for h in range(w.H)])
+                         for b in range(w.B)])
+        o_ref, l_ref = attention_fp64(q, k, v, w.scale, causal=w.causal, rows=rows)
+        bi = np.arange(w.B)[:, None, None]
+        hi = np.arange(w.H)[None, :, None]
+        og = out.cpu().numpy()[bi, hi, rows].astype(np.float64)
+        lg = lse.cpu().numpy()[bi, hi, rows].astype(np.float64)
+        d_o = np.abs(og - o_ref)
+        d_l = np.abs(lg - l_ref) / np.maximum(np.abs(l_ref), 1)
+        result["parity"] = {"rows_per_head": 64, "max_abs_dO": float(d_o.max()),
+                            "mean_abs_dO": float(d_o.mean()), "max_rel_dLSE": float(d_l.max()),
+                            "pass": bool(d_o.max() <= 4e-3 and d_o.mean() <= 5e-4 and d_l.max() <= 1e-4)}
+        log(f"[bench] parity {result['parity']}")
+
+    if args.no_cpu_baseline:
+        result["cpu_baseline"] = None
+    else:
+        log("[bench] timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        log(f"[bench] cpu baseline {result['cpu_baseline']}")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""FlashAttention-2 forward pass for AMD MI355X (gfx950).
+
+``fwd(q, k, v, scale=None, causal=False) -> (o, lse)`` runs the library's
+hand-written gfx950 kernels on torch fp16 tensors; ``fa2_fwd`` is the C entry
+point itself (raw device addresses).  The seeded synthetic workloads live in
+``exact_attention_fwd_amd.workloads``.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    FA2_ERR_INVALID_ARG,
+    FA2_ERR_LAUNCH,
+    FA2_ERR_MISALIGNED,
+    FA2_ERR_NO_DEVICE,
+    FA2_ERR_UNSUPPORTED,
+    FA2_OK,
+    LIB_PATH,
+    Fa2Error,
+    fa2_fwd,
+    fa2_last_hip_error,
+    fa2_status_string,
+    fa2_version,
+    fwd,
+    load_library,
+)

@@ -1,0 +1,56 @@
+"""Compile libfa2.so (the C-ABI library with the gfx950 kernels) in-tree.
+
+    python -m exact_attention_fwd_amd._build [--resource-usage]
+
+Every HIP translation unit is built for gfx950 only, with packed-FP32 ops
+disabled (the host pass warns that it does not know the feature; harmless).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libfa2.so")
+SOURCES = [os.path.join(CSRC, "fa2_api.cpp"), os.path.join(CSRC, "fa2_fwd_gfx950.hip")]
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: a ROCm toolchain is needed to build libfa2")
+    return path
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    """Build libfa2.so next to this file and return its path (always rebuilds)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    if resource_usage:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    log = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "is not a recognized feature for this target" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"libfa2 build failed:\n{' '.join(cmd)}\n{log}")
+    if verbose or resource_usage:
+        print(log)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, resource_usage="--resource-usage" in sys.argv))

@@ -1,0 +1,79 @@
+// C-ABI entry points of libfa2 (declared in include/fa2.h).
+//
+// Every argument check runs before the first HIP call, so argument errors are
+// reported the same way on a machine without a GPU.
+#include "fa2.h"
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "fa2_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+
+}  // namespace
+
+extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int H, int N, int d, float scale,
+                       int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
+    // Per-head byte offsets are 32-bit buffer offsets: N * d * 2 plus one
+    // tile of prefetch must stay below 2^31.
+    if (N > (1 << 22)) return FA2_ERR_INVALID_ARG;
+    const int64_t rows = int64_t(B) * H * N;
+    if (rows > INT32_MAX) return FA2_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA2_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(lse);
+    if (bits & 15u) return FA2_ERR_MISALIGNED;
+    const size_t t_bytes = size_t(rows) * size_t(d) * 2;
+    const size_t l_bytes = size_t(rows) * 4;
+    for (const void* in : {q, k, v}) {
+        if (overlaps(o, t_bytes, in, t_bytes) || overlaps(lse, l_bytes, in, t_bytes))
+            return FA2_ERR_INVALID_ARG;
+    }
+    if (overlaps(lse, l_bytes, o, t_bytes)) return FA2_ERR_INVALID_ARG;
+
+    const hipError_t err = fa2::launch_fwd(q, k, v, o, lse, B * H, N, d, scale, causal != 0,
+                                           static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) return FA2_OK;
+    g_last_hip_error = static_cast<int>(err);
+    switch (err) {
+        case hipErrorNoDevice:
+        case hipErrorInvalidDevice:
+        case hipErrorInsufficientDriver:
+        case hipErrorNoBinaryForGpu:
+        case hipErrorNotInitialized:
+            return FA2_ERR_NO_DEVICE;
+        default:
+            return FA2_ERR_LAUNCH;
+    }
+}
+
+extern "C" const char* fa2_status_string(int status) {
+    switch (status) {
+        case FA2_OK: return "ok";
+        case FA2_ERR_INVALID_ARG: return "invalid argument";
+        case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
+        case FA2_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case FA2_ERR_NO_DEVICE: return "no usable gfx950 device";
+        case FA2_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int fa2_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" const char* fa2_version(void) { return "fa2-gfx950 0.1.0"; }

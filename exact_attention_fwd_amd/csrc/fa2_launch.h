@@ -1,0 +1,14 @@
+// Internal interface between the C-ABI entry point (argument checks) and the
+// gfx950 kernels.  Not installed; the public interface is include/fa2.h.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace fa2 {
+
+// Launch the forward kernel for already-validated arguments.  Returns the
+// HIP error of the launch (hipSuccess on success).
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o,
+                      float* lse, int BH, int N, int d, float scale,
+                      bool causal, hipStream_t stream);
+
+}  // namespace fa2

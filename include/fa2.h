@@ -1,0 +1,86 @@
+/*
+ * fa2.h -- C ABI of the FlashAttention-2 forward pass for AMD MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention of one head, for every
+ * (batch, head) pair:
+ *
+ *     O   = softmax(scale * Q K^T) V            (row-wise softmax)
+ *     LSE = m + ln(l),  m = max_j s_ij,  l = sum_j exp(s_ij - m)
+ *
+ * Definitions: "3.6 Attention I -- the memory problem and FlashAttention
+ * principles", sections 3.6.2 (scaled dot-product attention), 3.6.4 (stable
+ * softmax and the online recurrence) and 3.6.7 (the row statistic
+ * L = m + log l kept for the backward pass); "FlashAttention-2 from scratch
+ * in CuTe", kernel-structure section (P = Q K^T / sqrt(d_h), fp16 inputs,
+ * fp32 accumulation).  The causal option masks future keys as in 3.6.6 of
+ * the first page.  The N x N score matrix is never written to memory: the
+ * kernel walks key/value tiles with the online-softmax recurrence and
+ * normalises once at the end.
+ *
+ * All functions are plain C, thread-safe and re-entrant; the library keeps no
+ * state between calls and allocates no device memory.
+ */
+#ifndef FA2_H_
+#define FA2_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by fa2_fwd. */
+typedef enum {
+    FA2_OK = 0,
+    FA2_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, grid too large,
+                                non-finite scale, output aliasing an input     */
+    FA2_ERR_UNSUPPORTED = 2, /* head dim other than 64 or 128                  */
+    FA2_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned                  */
+    FA2_ERR_NO_DEVICE = 4,   /* no usable gfx950 device / HIP runtime failure  */
+    FA2_ERR_LAUNCH = 5       /* the kernel launch failed                       */
+} fa2_status;
+
+/*
+ * fa2_fwd -- attention forward pass, asynchronous on `stream`.
+ *
+ *   q, k, v : device pointers, fp16 (IEEE binary16), shape [B, H, N, d],
+ *             contiguous row-major (d fastest).  Read only.
+ *   o       : device pointer, fp16 [B, H, N, d], contiguous.  Written: every
+ *             element, O rounded once to fp16 (round to nearest even).
+ *   lse     : device pointer, fp32 [B, H, N].  Written: natural-log
+ *             log-sum-exp of the scaled scores of each query row over its
+ *             visible keys.
+ *   B, H, N : batch, heads, sequence length (queries = keys = N); each >= 1,
+ *             N <= 4194304 (2^22) and B * H * N <= 2^31 - 1.
+ *   d       : head dimension, 64 or 128.
+ *   scale   : softmax scale (normally 1/sqrt(d)); any finite value.  0 gives
+ *             uniform weights over the visible keys.
+ *   causal  : non-zero: query i sees keys j <= i only (top-left aligned).
+ *   stream  : a hipStream_t passed as void*; NULL means the null stream.
+ *
+ * Ownership: the caller allocates and owns all five buffers.  o and lse must
+ * not overlap q, k or v, nor each other (any overlap is rejected).  Alignment: all
+ * pointers 16-byte aligned.
+ *
+ * Errors: all argument checks run before the first HIP call, so a bad call
+ * returns FA2_ERR_INVALID_ARG / _UNSUPPORTED / _MISALIGNED without touching
+ * the device.  A failed launch returns FA2_ERR_LAUNCH (the HIP error code is
+ * then available from fa2_last_hip_error).  The call never prints, throws or
+ * synchronises; results are ready once the caller synchronises the stream.
+ * NaN or Inf inputs are outside the contract and propagate per IEEE rules.
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa2_status_string(int status);
+
+/* hipError_t of this thread's last FA2_ERR_LAUNCH / FA2_ERR_NO_DEVICE (0 if none). */
+int fa2_last_hip_error(void);
+
+/* Static version string of the library. */
+const char* fa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H_ */

@@ -1,0 +1,115 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/fa2.h declares, and rejects bad arguments before any HIP
+call (so no compute call is made here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_fwd_amd as fa2
+from exact_attention_fwd_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa2.LIB_PATH):
+        _build.build()
+    return fa2.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(fa2.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_version_and_status_strings(lib):
+    assert fa2.fa2_version().startswith("fa2-gfx950")
+    seen = set()
+    for st in range(6):
+        s = fa2.fa2_status_string(st)
+        assert s and s not in seen
+        seen.add(s)
+    assert fa2.fa2_status_string(99) == "unknown status"
+    assert fa2.fa2_last_hip_error() == 0
+
+
+# Fake, 16-byte aligned, non-overlapping "device" addresses: every call below
+# fails validation, which runs before the first HIP call.
+Q, K, V, O, L = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20
+GOOD = dict(B=1, H=1, N=16, d=64, scale=0.125, causal=0)
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, **kw):
+    a = dict(GOOD, **kw)
+    return fa2.fa2_fwd(q, k, v, o, lse, a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], 0)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointer(lib, which):
+    assert call(**{which: 0}) == fa2.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("N", 0), ("B", -1), ("N", (1 << 22) + 1)])
+def test_bad_sizes(lib, field, value):
+    assert call(**{field: value}) == fa2.FA2_ERR_INVALID_ARG
+
+
+def test_too_many_rows(lib):
+    assert call(B=1024, H=1024, N=4096) == fa2.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_non_finite_scale(lib, scale):
+    assert call(scale=scale) == fa2.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [0, 32, 63, 96, 256])
+def test_unsupported_head_dim(lib, d):
+    assert call(d=d) == fa2.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_misaligned(lib, which):
+    base = dict(q=Q, k=K, v=V, o=O, lse=L)
+    assert call(**{which: base[which] + 8}) == fa2.FA2_ERR_MISALIGNED
+
+
+def test_overlapping_outputs(lib):
+    assert call(o=Q) == fa2.FA2_ERR_INVALID_ARG
+    assert call(o=K + 1024) == fa2.FA2_ERR_INVALID_ARG          # inside k's 2 KiB
+    assert call(lse=V + 16) == fa2.FA2_ERR_INVALID_ARG
+    assert call(lse=O + 2032) == fa2.FA2_ERR_INVALID_ARG        # inside o
+
+
+def test_python_wrapper_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa2.fwd(x, x, x)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from exact_attention_fwd_amd import _lib
+    saved = _lib._lib
+    try:
+        _lib._lib = None
+        with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+            _lib.load_library(str(tmp_path / "libfa2.so"))
+    finally:
+        _lib._lib = saved

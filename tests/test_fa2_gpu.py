@@ -1,0 +1,206 @@
+"""GPU parity: the HIP attention forward against the float64 CPU oracle, on the
+same seeded inputs, through the C ABI (python binding -> libfa2.so).
+
+Workloads: the five configurations of the pages' shapes (tiny, [4,32,2048,64]
+non-causal and causal, [2,16,16384,128], [1,16,65536,128] non-causal and
+causal) plus [4,32,2048,128]; large ones are checked on 512 seeded query rows
+per (batch, head) and, for every element, on properties that hold at any
+size (finiteness, closed forms).  Edge cases: the pages' worked example
+embedded in d = 64, odd N (tails), stress inputs that move the running max,
+scale 0 / negative, determinism, NaN-poisoned and guard-banded outputs.
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+
+from exact_attention_fwd_amd.workloads import WORKLOADS, make_qkv, sample_rows, stress_inputs
+from oracle import attention_fp64
+from parity import diff, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(B, H, N, d, sigma, seed):
+    return make_qkv(B, H, N, d, sigma, seed)
+
+
+def check(name, q, k, v, scale, causal, rows=None):
+    o, l = run_gpu(q, k, v, scale, causal)
+    assert np.all(np.isfinite(o.astype(np.float32))) and np.all(np.isfinite(l)), name
+    if rows is None:
+        o_ref, l_ref = attention_fp64(q, k, v, scale, causal=causal)
+        og, lg = o, l
+    else:
+        o_ref, l_ref = attention_fp64(q, k, v, scale, causal=causal, rows=rows)
+        bi = np.arange(q.shape[0])[:, None, None]
+        hi = np.arange(q.shape[1])[None, :, None]
+        og, lg = o[bi, hi, rows], l[bi, hi, rows]
+    dd = diff(og, lg, o_ref, l_ref)
+    say(f"[parity] {name}: {dd}")
+    assert dd.ok(), f"{name}: {dd}"
+    return o, l
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("name", ["tiny", "ref", "ref_causal"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    q, k, v = inputs(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    check(name, q, k, v, w.scale, w.causal)
+
+
+def test_tiny_causal():
+    w = WORKLOADS["tiny"]
+    q, k, v = inputs(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    check("tiny_causal", q, k, v, w.scale, True)
+
+
+@pytest.mark.parametrize("name", ["ref_d128", "hd128_16k", "long_64k", "long_64k_causal"])
+def test_workload_sampled(name):
+    w = WORKLOADS[name]
+    q, k, v = inputs(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    rows = np.stack([np.stack([sample_rows(w.N, b, h, w.sampled_rows) for h in range(w.H)])
+                     for b in range(w.B)])
+    check(name, q, k, v, w.scale, w.causal, rows=rows)
+
+
+# ------------------------------------------------ the pages' worked examples
+def _embed(scores, values, d=64):
+    """One head whose every query row has exactly the given scores (scale 1)."""
+    n = len(scores)
+    q = np.zeros((1, 1, n, d), np.float16)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    q[..., 0] = 1
+    k[0, 0, :, 0] = scores
+    v[0, 0, :, 0] = values
+    return q, k, v
+
+
+def test_worked_example_in_d64():
+    # "Attention I", 3.6.5: scores [1,3,2,5], values [10,20,30,40] -> 36.88,
+    # l = 1.2034.  fp16 rounds 36.880566 to 36.875 (far from the midpoint).
+    q, k, v = _embed([1, 3, 2, 5], [10, 20, 30, 40])
+    o, l = run_gpu(q, k, v, 1.0, False)
+    assert np.all(o[..., 0] == np.float16(36.875)), o[..., 0]
+    assert np.all(o[..., 1:] == 0)
+    lse = 5.0 + math.log(1 + math.exp(-4) + math.exp(-2) + math.exp(-3))
+    np.testing.assert_allclose(l, lse, rtol=1e-6)
+    # causal: row 0 sees only key 0 -> exactly v_0 and LSE = s_00 = 1
+    o, l = run_gpu(q, k, v, 1.0, True)
+    assert o[0, 0, 0, 0] == 10 and l[0, 0, 0] == pytest.approx(1.0, abs=1e-6)
+
+
+def test_exercise2_constant_values_in_d64():
+    # "Attention I", 3.6.11 exercise 2: scores [0,2,4], all values 1 -> O = 1.
+    q, k, v = _embed([0, 2, 4], [1, 1, 1])
+    o, l = run_gpu(q, k, v, 1.0, False)
+    assert np.all(np.abs(o[..., 0].astype(np.float64) - 1.0) <= 2.0 ** -10)
+    np.testing.assert_allclose(l, 4 + math.log(1 + math.exp(-2) + math.exp(-4)), rtol=1e-6)
+
+
+# -------------------------------------------------------------- tails, odd N
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 4, 17, 63, 65, 129, 1000])
+def test_odd_lengths(n, d, causal):
+    q, k, v = make_qkv(1, 2, n, d, 1.0, seed=n)
+    check(f"N={n} d={d} causal={causal}", q, k, v, d ** -0.5, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_batch_heads_and_ragged_tail_together(d):
+    q, k, v = make_qkv(3, 5, 300, d, 1.0, seed=7)
+    for causal in (False, True):
+        check(f"[3,5,300,{d}] causal={causal}", q, k, v, d ** -0.5, causal)
+
+
+# ----------------------------------------------------------- stress inputs
+@pytest.mark.parametrize("kind", ["rising", "falling", "large", "const_v", "zero_q"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_stress(kind, d, causal):
+    q, k, v = stress_inputs(kind, 1, 2, 333, d, seed=3)
+    check(f"stress {kind} d={d} causal={causal}", q, k, v, 1.0 if kind in ("rising", "falling") else d ** -0.5,
+          causal)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.3, 1e-3])
+def test_scale_values(scale):
+    q, k, v = make_qkv(1, 2, 200, 64, 1.0, seed=11)
+    for causal in (False, True):
+        check(f"scale={scale} causal={causal}", q, k, v, scale, causal)
+
+
+# ----------------------------------------- full-size properties, every element
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_size_closed_forms(causal):
+    """[1,16,65536,128]: with Q = 0 every weight is equal, so LSE is ln of the
+    visible-key count for every row; with constant V every output is that V."""
+    w = WORKLOADS["long_64k"]
+    _, k, v = inputs(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    q0 = np.zeros_like(k)
+    o, l = run_gpu(q0, k, v, w.scale, causal)
+    n_vis = np.arange(1, w.N + 1) if causal else np.full(w.N, w.N)
+    np.testing.assert_allclose(l, np.broadcast_to(np.log(n_vis), l.shape), rtol=2e-6)
+    if causal:
+        assert np.array_equal(o[:, :, 0], v[:, :, 0])   # row 0 sees key 0 only
+    vc = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    qq, _, _ = inputs(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    o, l = run_gpu(qq, k, vc, w.scale, causal)
+    err = np.abs(o.astype(np.float32) - vc.astype(np.float32))
+    say(f"[parity] full-size constant V causal={causal}: max|O-v0|={err.max():.3e}")
+    assert err.max() <= 2 ** -11 * np.abs(vc).astype(np.float32).max() * 2
+    assert np.all(np.isfinite(l))
+
+
+# ------------------------------------------------------ run-level guarantees
+def test_deterministic_and_overwrites_poisoned_outputs():
+    q, k, v = make_qkv(2, 4, 777, 128, 1.0, seed=5)
+    tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    import exact_attention_fwd_amd as fa2
+    for causal in (False, True):
+        out = torch.full_like(tq, float("nan"))
+        lse = torch.full((2, 4, 777), float("nan"), device="cuda")
+        o1, l1 = fa2.fwd(tq, tk, tv, causal=causal, out=out, lse=lse)
+        o2, l2 = fa2.fwd(tq, tk, tv, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o1.float()).all() and torch.isfinite(l1).all()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_guard_bands_untouched():
+    import exact_attention_fwd_amd as fa2
+    B, H, N, d, guard = 1, 3, 257, 64, 512
+    q, k, v = make_qkv(B, H, N, d, 1.0, seed=9)
+    tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    n_o, n_l = B * H * N * d, B * H * N
+    o_buf = torch.full((n_o + 2 * guard,), 7.0, dtype=torch.float16, device="cuda")
+    l_buf = torch.full((n_l + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    out = o_buf[guard:guard + n_o].view(B, H, N, d)
+    lse = l_buf[guard:guard + n_l].view(B, H, N)
+    fa2.fwd(tq, tk, tv, out=out, lse=lse, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[:guard] == 7) and torch.all(o_buf[guard + n_o:] == 7)
+    assert torch.all(l_buf[:guard] == 7) and torch.all(l_buf[guard + n_l:] == 7)
+    o_ref, l_ref = attention_fp64(q, k, v, d ** -0.5, causal=True)
+    dd = diff(out.cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref)
+    assert dd.ok(), str(dd)
+
+
+def test_runs_on_the_callers_stream():
+    import exact_attention_fwd_amd as fa2
+    q, k, v = make_qkv(1, 2, 512, 64, 1.0, seed=13)
+    tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    ref_o, ref_l = fa2.fwd(tq, tk, tv)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = fa2.fwd(tq, tk, tv)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
