@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead: run a plain device copy of MIB MiB five times (the known-size "
+                         "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,6 +122,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
 
     import exact_attention_fwd_amd as fa2
     from exact_attention_fwd_amd.workloads import WORKLOADS, make_qkv, sample_rows

@@ -29,7 +29,7 @@
 //    MFMA (O^T = V^T P^T), so P never leaves registers; V^T comes from LDS
 //    through ds_read_b64_tr_b16, which returns four consecutive keys of one
 //    head-dim column per lane.  The rescale of acc by alpha is a per-lane
-//    scalar multiply, skipped when alpha == 1 on every lane of the wave.
+//    scalar multiply.
 //  * K and V tiles (64 keys) are double-buffered in LDS.  The next tile's K
 //    is fetched (128-bit buffer loads) before this tile's QK^T and written to
 //    LDS after it; the next V is fetched then and written after this tile's
@@ -64,6 +64,9 @@ constexpr int kQW = 32;             // query rows per wave
 constexpr int kBQ = kWaves * kQW;   // query rows per workgroup
 constexpr int kBK = 64;             // keys per K/V tile
 constexpr float kLn2 = 0.69314718055994530942f;
+// Largest growth of a row's scaled max (log2 units) the fast loop absorbs
+// without rescaling: its fp16 weights stay <= 2^8.
+constexpr float kLazy = 8.0f;
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
 
 template <int D>
@@ -191,7 +194,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     f32x16 oacc[C::kDBlocks];
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db) oacc[db] = f32x16{};
-    float m2 = -INFINITY;   // running max of c*S for this query (log2 units)
+    float m2 = -INFINITY;   // reference max of c*S for this query (log2 units)
     float lsum = 0.f;       // this lane's share of the running sum
 
     // Per-lane LDS read bases; the unrolled loops add compile-time offsets.
@@ -208,6 +211,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 
     // S^T = K Q^T for 64 keys x 32 queries: two 32x32 accumulators.
     auto qk_tile = [&](int buf, f32x16 (&s)[2]) {
+        __builtin_amdgcn_s_setprio(1);
         const unsigned char* kbuf = kbuf_of(buf);
         s[0] = f32x16{};
         s[1] = f32x16{};
@@ -219,48 +223,52 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ds], s[kb], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
-    // Online-softmax update and O^T += V^T P^T for one tile.  MASK selects
-    // the path for tiles that cross the causal diagonal or hold keys beyond
-    // N; every other tile runs without per-element compares.
-    auto softmax_pv_tile = [&](auto mask_tag, int buf, int k0, f32x16 (&s)[2]) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        if constexpr (MASK) {
+    // Keys beyond N, and on diagonal tiles keys after the query, get -inf.
+    // Register r of accumulator kb holds key k0 + 4*hi + off(kb, r) with a
+    // compile-time off, so each test is one per-lane base against a constant.
+    auto mask_tile = [&](int k0, f32x16 (&s)[2]) {
+        const int past_end = k0 + 4 * hi - N;      // key >= N  <=>  past_end + off >= 0
+        const int after_q = k0 + 4 * hi - my_q;    // key > q   <=>  after_q + off > 0
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool vis = key < N && (!CAUSAL || key <= my_q);
-                    if (!vis) s[kb][r] = -INFINITY;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+                const bool hidden = past_end >= -off || (CAUSAL && after_q > -off);
+                if (hidden) s[kb][r] = -INFINITY;
             }
         }
+    };
 
-        float mx = s[0][0];
+    // Row max of the tile's 64 scores of this lane's query: 32 in-lane values
+    // as a shallow v_max3 tree, then one swap with lane l^32.
+    auto tile_max = [&](const f32x16 (&s)[2]) {
+        float t[11];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[1][r]);
-        mx = pair_max(mx);
-        float m2_new, shift;
-        if constexpr (MASK) {
-            // A row with nothing visible yet keeps shift 0, so that
-            // -inf - (-inf) never occurs; its weights are all zero.
-            const float m2_tile = (mx == -INFINITY) ? -INFINITY : c * mx;
-            m2_new = __builtin_fmaxf(m2, m2_tile);
-            shift = (m2_new == -INFINITY) ? 0.f : m2_new;
-        } else {
-            m2_new = __builtin_fmaxf(m2, c * mx);
-            shift = m2_new;
+        for (int i = 0; i < 10; ++i) {
+            const int r0 = 3 * i;
+            t[i] = __builtin_fmaxf(__builtin_fmaxf(s[r0 >> 4][r0 & 15], s[(r0 + 1) >> 4][(r0 + 1) & 15]),
+                                   s[(r0 + 2) >> 4][(r0 + 2) & 15]);
         }
-        const float alpha = __builtin_amdgcn_exp2f(m2 - shift);
-        m2 = m2_new;
+        t[10] = __builtin_fmaxf(s[1][14], s[1][15]);
+        const float u0 = __builtin_fmaxf(__builtin_fmaxf(t[0], t[1]), t[2]);
+        const float u1 = __builtin_fmaxf(__builtin_fmaxf(t[3], t[4]), t[5]);
+        const float u2 = __builtin_fmaxf(__builtin_fmaxf(t[6], t[7]), t[8]);
+        const float u3 = __builtin_fmaxf(t[9], t[10]);
+        return pair_max(__builtin_fmaxf(__builtin_fmaxf(u0, u1), __builtin_fmaxf(u2, u3)));
+    };
 
-        // P = exp2(c*S - m2); the row sum uses fp32 P, the MFMA fp16 (RNE) P.
-        h8 pf[4];
-        float rs = 0.f;
+    // P = exp2(c*S - shift) rounded to fp16 (RNE) as the B operands of the
+    // PV MFMA; returns this lane's share of the row sum of the fp32 weights
+    // (4 independent add chains).  Summing the fp16-rounded weights instead
+    // would put up to 2^-12 relative error per term into l, which short
+    // (causal) rows pass straight on to the LSE.
+    auto exp_tile = [&](auto mask_tag, const f32x16 (&s)[2], float shift, h8 (&pf)[4]) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -268,22 +276,17 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                 const float x = s[kb][r];
                 float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -shift));
                 if constexpr (MASK) p = (x == -INFINITY) ? 0.f : p;
-                rs += p;
+                rsum[r & 3] += p;
                 pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
             }
         }
-        lsum = alpha * lsum + rs;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-            // In place (tied operands), so the skipped path needs no copy.
-#pragma unroll
-            for (int db = 0; db < C::kDBlocks; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    asm volatile("v_mul_f32 %0, %1, %0" : "+v"(oacc[db][r]) : "v"(alpha));
-        }
+        return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+    };
 
-        // O^T += V^T P^T: 4 k-steps of 16 keys, D/32 row blocks.
+    // O^T += V^T P^T: 4 k-steps of 16 keys, D/32 row blocks.
+    auto pv_tile = [&](int buf, const h8 (&pf)[4]) {
         const unsigned char* vbuf = vbuf_of(buf);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -295,6 +298,15 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], oacc[db], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // Causal: a tile entirely in this wave's future has no work; tiles that
+    // cross the diagonal or the end of the sequence are masked.
+    auto active = [&](int kt) { return !CAUSAL || kt * kBK <= qw0 + kQW - 1; };
+    auto needs_mask = [&](int kt) {
+        const int k0 = kt * kBK;
+        return (CAUSAL && k0 + kBK - 1 > qw0) || (k0 + kBK > N);
     };
 
     load_rows(rK, 0);
@@ -303,26 +315,73 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     store_rows(vbuf_of(0), v_st);
     __syncthreads();
 
-    // Each iteration also moves the next tile into the other LDS buffer; past
-    // the last tile the buffer loads return zeros and nothing reads them.
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // The recurrence, with a lazily updated reference max m2.  Every tile
+    // also moves the next tile into the other LDS buffers (past the last tile
+    // the buffer loads return zeros and nothing reads them) and ends in one
+    // barrier.
+    //
+    // Fast loop: unmasked tiles whose scaled row max stays within kLazy of
+    // m2.  They take P = exp2(c*S - m2) <= 2^kLazy against the unchanged m2,
+    // so acc and l need no rescale (alpha = 1) and no mask.
+    // General path: everything else -- the first tile, diagonal and tail
+    // tiles, and a tile whose max outgrows m2 + kLazy.  There m2 becomes the
+    // running max exactly as in the recurrence, acc and l are rescaled by
+    // alpha = exp2(m2_old - m2_new), and the loop is re-entered.
+    // Both give the same softmax: only the common shift of a row differs.
+    int kt = 0;
+    f32x16 s[2];
+    while (kt < n_kt) {
+        bool mid_tile = false;   // left the fast loop after this tile's QK^T
+        for (; kt < n_kt; ++kt) {
+            if (!active(kt) || needs_mask(kt)) break;
+            const int buf = kt & 1;
+            load_rows(rK, kt + 1);
+            qk_tile(buf, s);
+            store_rows(kbuf_of(buf ^ 1), k_st);
+            load_rows(rV, kt + 1);
+            const float m2_tile = c * tile_max(s);
+            if (__builtin_amdgcn_ballot_w64(m2_tile > m2 + kLazy)) {
+                mid_tile = true;
+                break;
+            }
+            h8 pf[4];
+            lsum += exp_tile(std::false_type{}, s, m2, pf);
+            pv_tile(buf, pf);
+            store_rows(vbuf_of(buf ^ 1), v_st);
+            __syncthreads();
+        }
+        if (kt >= n_kt) break;
+
         const int buf = kt & 1;
-        const int k0 = kt * kBK;
-        // Causal: a tile entirely in this wave's future is skipped; tiles
-        // crossing the diagonal or the end of the sequence are masked.
-        const bool active = !CAUSAL || k0 <= qw0 + kQW - 1;
-        const bool need_mask = (CAUSAL && k0 + kBK - 1 > qw0) || (k0 + kBK > N);
-        load_rows(rK, kt + 1);
-        f32x16 s[2];
-        if (active) qk_tile(buf, s);
-        store_rows(kbuf_of(buf ^ 1), k_st);
-        load_rows(rV, kt + 1);
-        if (active) {
-            if (need_mask) softmax_pv_tile(std::true_type{}, buf, k0, s);
-            else softmax_pv_tile(std::false_type{}, buf, k0, s);
+        const bool act = active(kt);
+        if (!mid_tile) {
+            load_rows(rK, kt + 1);
+            if (act) qk_tile(buf, s);
+            store_rows(kbuf_of(buf ^ 1), k_st);
+            load_rows(rV, kt + 1);
+        }
+        if (act) {
+            const bool masked = needs_mask(kt);
+            if (masked) mask_tile(kt * kBK, s);
+            const float mx = tile_max(s);
+            // A row with nothing visible yet keeps shift 0, so that
+            // -inf - (-inf) never occurs; its weights are all zero.
+            const float m2_tile = (mx == -INFINITY) ? -INFINITY : c * mx;
+            const float m2_new = __builtin_fmaxf(m2, m2_tile);
+            const float shift = (m2_new == -INFINITY) ? 0.f : m2_new;
+            const float alpha = __builtin_amdgcn_exp2f(m2 - shift);
+            m2 = m2_new;
+#pragma unroll
+            for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
+            h8 pf[4];
+            // the masked variant is also right for unmasked tiles (no -inf)
+            const float rs = exp_tile(std::true_type{}, s, shift, pf);
+            lsum = alpha * lsum + rs;
+            pv_tile(buf, pf);
         }
         store_rows(vbuf_of(buf ^ 1), v_st);
         __syncthreads();
+        ++kt;
     }
 
     // Epilogue: one normalisation, fp16 (RNE) O, natural-log LSE.

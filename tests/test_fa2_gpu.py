@@ -204,3 +204,22 @@ def test_runs_on_the_callers_stream():
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jump", [3.0, 20.0])
+def test_row_max_jumps_mid_sequence(d, causal, jump):
+    """Scores ~0 except one key per row block far into the sequence whose score
+    jumps by `jump` (natural units).  A jump of 20 (29 in log2 units) forces a
+    rescale in the middle of the key loop; a jump of 3 (4.3 in log2 units) is
+    absorbed without one.  Both must give the same softmax as the oracle."""
+    n = 2048
+    q, k, v = make_qkv(1, 2, n, d, 1.0, seed=17)
+    q = (q.astype(np.float32) * 0.05).astype(np.float16)
+    q[..., 0] = 1.0
+    k = (k.astype(np.float32) * 0.05).astype(np.float16)
+    k[..., 0] = 0.0
+    k[:, :, 1500, 0] = jump
+    k[:, :, 700, 0] = jump / 2
+    check(f"jump={jump} d={d} causal={causal}", q, k, v, 1.0, causal)
