@@ -28,8 +28,18 @@
 //  * The accumulator's register order is reused as the B operand of the PV
 //    MFMA (O^T = V^T P^T), so P never leaves registers; V^T comes from LDS
 //    through ds_read_b64_tr_b16, which returns four consecutive keys of one
-//    head-dim column per lane.  The rescale of acc by alpha is a per-lane
-//    scalar multiply.
+//    head-dim column per lane.
+//  * The key loop has a fast path and a general path.  The fast loop runs
+//    unmasked tiles whose scaled row max stays within kLazy (log2 units) of
+//    a lazily updated reference max m2: their weights exp2(S*c - m2) are at
+//    most 2^kLazy, so acc and l need no rescale and no mask.  Everything
+//    else (first tile, diagonal and tail tiles, a tile whose max outgrows
+//    m2 + kLazy) takes the general path, which sets m2 to the running max as
+//    in the recurrence and rescales acc and l by alpha = exp2(m2_old -
+//    m2_new).  The softmax is the same: a row's common shift cancels.
+//  * In the fast loop P and P V are software-pipelined over the 4 k-steps
+//    of 16 keys: the MFMAs of one step overlap the LDS reads and the
+//    exponentials of the next.
 //  * K and V tiles (64 keys) are double-buffered in LDS.  The next tile's K
 //    is fetched (128-bit buffer loads) before this tile's QK^T and written to
 //    LDS after it; the next V is fetched then and written after this tile's
@@ -40,6 +50,7 @@
 //  * Workgroup ids are remapped so that all Q tiles of one head run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2;
 //    causal grids start with the longest rows.
+//  * Occupancy: 3 waves per SIMD at d = 64, 2 at d = 128 (register bound).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -115,8 +126,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
 }
 
+// Occupancy: d = 64 fits 3 waves per SIMD (<= 168 VGPRs), d = 128 needs
+// the 256 VGPRs of 2 waves per SIMD.
+template <int D>
+constexpr int kWavesPerEU = D == 64 ? 3 : 2;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>, kWavesPerEU<D>)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
                     float* __restrict__ LSE, int N, int n_qtiles, int n_wg, float c,
@@ -301,6 +318,46 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         __builtin_amdgcn_s_setprio(0);
     };
 
+    // Fast-loop P and P V, software-pipelined over the 4 k-steps of 16
+    // keys: while the MFMAs of step ks run, the V^T operands of step ks+1
+    // are read from LDS and its 8 weights per lane are exponentiated.
+    auto exp_pv_pipelined = [&](int buf, const f32x16 (&s)[2], float shift) {
+        const unsigned char* vbuf = vbuf_of(buf);
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+        auto exp_step = [&](int ks, h8& pk) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = s[ks >> 1][8 * (ks & 1) + j];
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -shift));
+                rsum[j & 3] += p;
+                pk[j] = (_Float16)p;
+            }
+        };
+        auto read_step = [&](int ks, h8 (&va)[C::kDBlocks]) {
+#pragma unroll
+            for (int db = 0; db < C::kDBlocks; ++db) {
+                const int imm = ((4 * db) * 64 + 16 * ks) << 4;
+                const h4 ta = lds_read_tr(vbuf + v_base0 + imm);
+                const h4 tb = lds_read_tr(vbuf + v_base1 + imm);
+                va[db] = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        h8 va[2][C::kDBlocks];
+        h8 pk[2];
+        read_step(0, va[0]);
+        exp_step(0, pk[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) read_step(ks + 1, va[(ks + 1) & 1]);
+#pragma unroll
+            for (int db = 0; db < C::kDBlocks; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks & 1][db], pk[ks & 1], oacc[db], 0, 0, 0);
+            if (ks + 1 < 4) exp_step(ks + 1, pk[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+    };
+
     // Causal: a tile entirely in this wave's future has no work; tiles that
     // cross the diagonal or the end of the sequence are masked.
     auto active = [&](int kt) { return !CAUSAL || kt * kBK <= qw0 + kQW - 1; };
@@ -344,9 +401,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                 mid_tile = true;
                 break;
             }
-            h8 pf[4];
-            lsum += exp_tile(std::false_type{}, s, m2, pf);
-            pv_tile(buf, pf);
+            lsum += exp_pv_pipelined(buf, s, m2);
             store_rows(vbuf_of(buf ^ 1), v_st);
             __syncthreads();
         }
