@@ -35,16 +35,20 @@
 //    (both independent of tile t's softmax) interleaved slot by slot with the
 //    softmax of tile t on the VALU.  The per-element VALU chain (scaled
 //    score -> exp2 -> row sum and fp16 conversion) is itself pipelined across
-//    slots, so no instruction waits on the one just issued; the row max and
-//    the reference-max update take the first four slots.  S^T is
+//    slots, so no instruction waits on the one just issued.  S^T is
 //    double-buffered in registers by tile parity; P is single-buffered: the
 //    P V MFMAs come first in the stream and each 16-key chunk of P is
 //    rewritten only after its last reader has issued.
-//  * Lazy reference max, per row: m2 moves to the tile's scaled max only when
-//    that exceeds m2 by more than kLazy (log2 units); otherwise alpha = 1 and
-//    the weights exp2(S*c - m2) stay below 2^kLazy.  A row's common shift
-//    cancels in the softmax, so the result is the recurrence's; the wave
-//    rescales acc only when some row moved (ballot).
+//  * Lazy reference max, checked after the fact: the stream computes the
+//    weights exp2(S*c - m2) against the row's current reference m2 without a
+//    row max.  If the row's weights in the tile sum to at most 2^kLazy, each
+//    weight is at most 2^kLazy (safe in fp16) and m2 stays, alpha = 1.
+//    Otherwise (a weight may exceed 2^kLazy: the row max moved up, or m2 is
+//    not finite) the wave redoes the tile with the recurrence step
+//    itself: m2 := max(m2, scaled tile max), alpha = exp2(m2_old - m2_new),
+//    weights recomputed.  A row's common shift cancels in the softmax, so
+//    the result is the recurrence's; m2 starts at tile 0's max, and acc is
+//    rescaled only when some row of the wave moved (ballot).
 //  * K and V tiles (64 keys) are double-buffered in LDS and staged through
 //    registers: each iteration writes the tiles fetched during the previous
 //    one and fetches the next with 128-bit buffer loads spread one per slot
@@ -90,9 +94,9 @@ constexpr int kQW = 32;             // query rows per wave
 constexpr int kBQ = kWaves * kQW;   // query rows per workgroup (256)
 constexpr int kBK = 64;             // keys per K/V tile
 constexpr float kLn2 = 0.69314718055994530942f;
-// Largest lag (log2 units) of the reference max behind a tile's max before
-// the reference moves: weights stay <= 2^8, far inside fp16 range.
-constexpr float kLazy = 8.0f;
+// A tile keeps the row's reference max while the row's weights in it sum to
+// at most 2^kLazy, so every weight stays <= 2^8, far inside fp16 range.
+constexpr float kLazyBound = 256.0f;   // 2^kLazy, kLazy = 8
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kAhead = 4;                // LDS operand reads in flight ahead of the MFMAs
 
@@ -109,8 +113,8 @@ struct Cfg {
     static constexpr int kSlots = kPV + kQK;               // one MFMA per slot
     // Element pairs enter the three-stage VALU chain (scaled score, exp2,
     // sum + fp16) in slots [kE0, kE1); a pair's last stage runs two slots
-    // after its first.  Slots 0-3 hold the row max and the m2 update.
-    static constexpr int kE0 = 4;
+    // after its first.
+    static constexpr int kE0 = D == 128 ? 2 : 0;
     static constexpr int kE1 = kSlots - 2;
     static constexpr int pair_begin(int p) {
         return p <= kE0 ? 0 : p >= kE1 ? 16 : ((p - kE0) * 16) / (kE1 - kE0);
@@ -296,6 +300,14 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             }
         }
     }
+    // Reference max from tile 0, so the first iteration needs no correction.
+    if (0 >= n_full) mask_tile(0, s0);
+    {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) mx = __builtin_fmaxf(mx, s0[i >> 4][i & 15]);
+        m2 = c * pair_max(mx);
+    }
     __syncthreads();   // K buffer 0 is free before the first iteration refills it
 
     // Iteration t (PAR = t & 1).  Buffers: K(t+1) and V(t-1) are read from
@@ -344,42 +356,14 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             }
         };
 
-        // Softmax of tile t, one slice per slot.
-        float tm[11], u[4], mx = 0.f, shift = 0.f, rsum[4] = {0.f, 0.f, 0.f, 0.f};
+        // Softmax of tile t against the current reference max, one slice per
+        // slot; checked after the stream.
+        const float shift = m2;
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
         float arg[32], pe[32];
         auto sv = [&](int i) { return s_cur[i >> 4][i & 15]; };
         auto pb = [&](int p) { return p < 0 ? 0 : C::pair_begin(p); };
         auto valu = [&](int p) {
-            if (p == 0) {
-#pragma unroll
-                for (int i = 0; i < 10; ++i) {
-                    tm[i] = __builtin_fmaxf(__builtin_fmaxf(sv(3 * i), sv(3 * i + 1)), sv(3 * i + 2));
-                    pin(tm[i]);
-                }
-                tm[10] = __builtin_fmaxf(sv(30), sv(31));
-                pin(tm[10]);
-            } else if (p == 1) {
-                u[0] = __builtin_fmaxf(__builtin_fmaxf(tm[0], tm[1]), tm[2]);
-                u[1] = __builtin_fmaxf(__builtin_fmaxf(tm[3], tm[4]), tm[5]);
-                u[2] = __builtin_fmaxf(__builtin_fmaxf(tm[6], tm[7]), tm[8]);
-                u[3] = __builtin_fmaxf(tm[9], tm[10]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pin(u[i]);
-            } else if (p == 2) {
-                mx = pair_max(__builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), __builtin_fmaxf(u[2], u[3])));
-                pin(mx);
-            } else if (p == 3) {
-                // c > 0, so a fully masked tile gives m2_tile = -inf and
-                // leaves m2 alone.  A row that has seen no key keeps shift
-                // 0 (so -inf - (-inf) never occurs); its weights are 0.
-                const float m2_tile = c * mx;
-                const float m2_new = m2_tile > m2 + kLazy ? m2_tile : m2;
-                shift = m2_new == -INFINITY ? 0.f : m2_new;
-                alpha = __builtin_amdgcn_exp2f(m2 - shift);
-                m2 = m2_new;
-                pin(shift);
-                pin(alpha);
-            }
             // Stage 3: row sum and fp16 P of the pairs that entered two slots ago.
 #pragma unroll
             for (int j = pb(p - 2); j < pb(p - 1); ++j) {
@@ -412,10 +396,6 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                     pin(arg[e]);
                 }
             }
-            if (p == C::kSlots - 1) {
-                lsum = alpha * lsum + ((rsum[0] + rsum[1]) + (rsum[2] + rsum[3]));
-                pin(lsum);
-            }
         };
 
         // The stream: per slot, the LDS read kAhead jobs ahead, one MFMA,
@@ -435,6 +415,32 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             if (p % 2 == 1 && p / 2 >= C::kStage && p / 2 < 2 * C::kStage)
                 fetch1(stv[p / 2 - C::kStage], rV, t + 1, p / 2 - C::kStage);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // The tile's weights for this row sum to at most 2^kLazy: every
+        // weight is then <= 2^kLazy and the reference max stays.  Otherwise
+        // (the row max moved up, or m2 was still -inf) take the recurrence
+        // step exactly: m2 := max(m2, tile max), rescale, recompute.
+        const float part = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+        const float tot = pair_sum(part);
+        if (__builtin_amdgcn_ballot_w64(!(tot <= kLazyBound))) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) mx = __builtin_fmaxf(mx, sv(i));
+            const float m2_new = __builtin_fmaxf(m2, c * pair_max(mx));
+            const float sh = m2_new == -INFINITY ? 0.f : m2_new;
+            alpha = __builtin_amdgcn_exp2f(m2 - sh);
+            m2 = m2_new;
+            float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv(e), c, -sh));
+                r[e & 3] += pv;
+                pf[e >> 3][e & 7] = (_Float16)pv;
+            }
+            lsum = alpha * lsum + ((r[0] + r[1]) + (r[2] + r[3]));
+        } else {
+            alpha = 1.0f;
+            lsum += part;
         }
         __syncthreads();
     };
