@@ -3,6 +3,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ref]
 
+Without --warmup / --steps, W fills about 0.4 s and K about 0.25 s of
+launches (the GPU's clock needs ~0.1 s of load to settle; a short kernel
+timed from a cold start reads up to ~6 % slow); the JSON line reports the W
+and K actually run.
+
 A step is one fa2_fwd call: the whole hot path (load Q, stream K/V tiles,
 two MFMA contractions, online softmax, normalised O and LSE) over one batch
 of seeded synthetic fp16 inputs already resident in HBM.  Prints ONE JSON
@@ -103,8 +108,8 @@ def cpu_baseline(w, q, k, v, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: ~0.25 s worth)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: ~0.4 s worth)")
     ap.add_argument("--workload", default="ref")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,7 +161,20 @@ def main():
         if status != fa2.FA2_OK:
             raise RuntimeError(f"fa2_fwd: {fa2.fa2_status_string(status)}")
 
-    for _ in range(args.warmup):
+    # Size the default warm-up and timed loop from a few probe launches (they
+    # count as warm-up).
+    n_probe = 5
+    torch.cuda.synchronize(dev)
+    tp0 = time.perf_counter()
+    for _ in range(n_probe):
+        step()
+    torch.cuda.synchronize(dev)
+    t_one = max((time.perf_counter() - tp0) / n_probe, 1e-6)
+    if args.warmup is None:
+        args.warmup = max(20, math.ceil(0.4 / t_one))
+    if args.steps is None:
+        args.steps = max(10, math.ceil(0.25 / t_one))
+    for _ in range(max(0, args.warmup - n_probe)):
         step()
     torch.cuda.synchronize(dev)
 

@@ -15,9 +15,10 @@
 // (Q tile, batch*head) with the Q tile resident, a K/V prefetch ahead of use,
 // 128-bit loads, bank-spread shared tiles and row-owning warps.
 //
-//  * One workgroup = 8 waves = 256 queries of one (batch, head), one
-//    workgroup per CU (two waves per SIMD).  Each wave owns 32 whole query
-//    rows, so every row reduction stays inside the wave.
+//  * Each wave owns 32 whole query rows, so every row reduction stays inside
+//    the wave.  A workgroup is 8 waves (256 queries of one (batch, head), one
+//    workgroup per CU) at d = 128 and 4 waves (128 queries, two independent
+//    workgroups per CU) at d = 64; either way two waves share each SIMD.
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_f16 (A = 32 keys x 16 dims from LDS, B = Q^T held in
 //    registers for the whole loop).  In the 32x32 accumulator a lane then
@@ -51,8 +52,11 @@
 //    rescaled only when some row of the wave moved (ballot).
 //  * K and V tiles (64 keys) are double-buffered in LDS and staged through
 //    registers: each iteration writes the tiles fetched during the previous
-//    one and fetches the next with 128-bit buffer loads spread one per slot
-//    over the stream.  One barrier per tile.
+//    one and fetches the next with 128-bit buffer loads, one LDS store or one
+//    load per slot over the stream.  One barrier per tile.  In an 8-wave
+//    workgroup the waves 4-7, which lose issue arbitration to the older waves
+//    0-3 on the same SIMD, run the stream at raised priority so the two
+//    halves reach the barrier closer together.
 //  * All global accesses are buffer instructions on a per-head resource
 //    whose size is the head's N*d*2 bytes: rows past N read as zero and
 //    stores past N are dropped by the hardware, so the tail needs no branch.
@@ -88,10 +92,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;             // query rows per wave
-constexpr int kBQ = kWaves * kQW;   // query rows per workgroup (256)
 constexpr int kBK = 64;             // keys per K/V tile
 constexpr float kLn2 = 0.69314718055994530942f;
 // A tile keeps the row's reference max while the row's weights in it sum to
@@ -102,6 +103,10 @@ constexpr int kAhead = 4;                // LDS operand reads in flight ahead of
 
 template <int D>
 struct Cfg {
+    // Waves per workgroup (see the header): 8 at d = 128, 4 at d = 64.
+    static constexpr int kWaves = D == 64 ? 4 : 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBQ = kWaves * kQW;               // query rows per workgroup
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
     static constexpr int kTileBytes = kBK * kRowBytes;
@@ -125,7 +130,9 @@ struct Cfg {
         for (int p = 0; p < kSlots; ++p)
             for (int j = pair_begin(p); j < pair_begin(p + 1); ++j)
                 if (p + 2 <= kDBlocks * (j / 4) + kDBlocks - 1) return false;
-        return pair_begin(kSlots) == 16 && kStage >= 1 && 4 * kStage <= kSlots;
+        // The staging stores take slots 0, 2, .., 4*kStage-2 and the loads
+        // refilling the same registers slots 2*kStage+1, .., 6*kStage-1.
+        return pair_begin(kSlots) == 16 && kStage >= 1 && 6 * kStage - 1 < kSlots;
     }
 };
 
@@ -161,7 +168,7 @@ template <typename T>
 __device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(Cfg<D>::kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
@@ -186,7 +193,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
     int qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
     if (CAUSAL) qt = n_qtiles - 1 - qt;   // longest rows first
-    const int q0 = qt * kBQ;
+    const int q0 = qt * C::kBQ;
     const size_t head = size_t(bh) * size_t(N) * D;
     const uint32_t head_bytes = uint32_t(N) * C::kRowBytes;
     const auto rQ = make_rsrc(Q + head, head_bytes);
@@ -207,7 +214,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         qf[ds] = __builtin_bit_cast(h8, raw);
     }
 
-    const int kv_end = CAUSAL ? min(N, q0 + kBQ) : N;
+    const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : N;
     const int n_kt = (kv_end + kBK - 1) / kBK;
     // Tiles below n_full need no mask for any row of the workgroup.
     const int n_full = CAUSAL ? min(N / kBK, (q0 + 1) / kBK) : N / kBK;
@@ -216,18 +223,14 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // key row i of a tile; the LDS address follows the tile's layout.
     u32x4 stk[C::kStage], stv[C::kStage];
     auto fetch1 = [&](u32x4& dst, __amdgpu_buffer_rsrc_t r, int kt, int j) {
-        const int ch = wave + kWaves * j;
+        const int ch = wave + C::kWaves * j;
         dst = __builtin_amdgcn_raw_buffer_load_b128(r, (kt * kBK + lane) * C::kRowBytes + ch * 16, 0, 0);
     };
-    auto put_k = [&](unsigned char* buf, const u32x4 (&src)[C::kStage]) {
-#pragma unroll
-        for (int j = 0; j < C::kStage; ++j)
-            *reinterpret_cast<u32x4*>(buf + lds_k_off(wave + kWaves * j, lane)) = src[j];
+    auto put_k1 = [&](unsigned char* buf, const u32x4& src, int j) {
+        *reinterpret_cast<u32x4*>(buf + lds_k_off(wave + C::kWaves * j, lane)) = src;
     };
-    auto put_v = [&](unsigned char* buf, const u32x4 (&src)[C::kStage]) {
-#pragma unroll
-        for (int j = 0; j < C::kStage; ++j)
-            *reinterpret_cast<u32x4*>(buf + lds_v_off(wave + kWaves * j, lane)) = src[j];
+    auto put_v1 = [&](unsigned char* buf, const u32x4& src, int j) {
+        *reinterpret_cast<u32x4*>(buf + lds_v_off(wave + C::kWaves * j, lane)) = src;
     };
 
     f32x16 oacc[C::kDBlocks];
@@ -273,7 +276,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Prologue.  Both V buffers start zeroed: the first iteration's P V runs
     // with P = 0 on buffer 1.  K(0), K(1) go to LDS; K(2) and V(0) are
     // fetched for the first iteration to store.
-    for (int i = tid; i < C::kTileBytes / 16; i += kThreads) {
+    for (int i = tid; i < C::kTileBytes / 16; i += C::kThreads) {
         reinterpret_cast<u32x4*>(vb0)[i] = u32x4{0u, 0u, 0u, 0u};
         reinterpret_cast<u32x4*>(vb1)[i] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -282,8 +285,11 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         fetch1(stk[j], rK, 0, j);
         fetch1(stv[j], rK, 1, j);
     }
-    put_k(kb0, stk);
-    put_k(kb1, stv);
+#pragma unroll
+    for (int j = 0; j < C::kStage; ++j) {
+        put_k1(kb0, stk[j], j);
+        put_k1(kb1, stv[j], j);
+    }
 #pragma unroll
     for (int j = 0; j < C::kStage; ++j) {
         fetch1(stk[j], rK, 2, j);
@@ -325,8 +331,6 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 #pragma unroll
             for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
         }
-        put_k(kb_store, stk);
-        put_v(vb_store, stv);
         if (t >= n_full) mask_tile(t * kBK, s_cur);
 
         // MFMA job p: p < kPV is P V (k-step p / kDBlocks, O^T block
@@ -399,23 +403,30 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         };
 
         // The stream: per slot, the LDS read kAhead jobs ahead, one MFMA,
-        // the slot's VALU slice and at most one staging load (K(t+3) chunks
-        // in slots 1, 3, ..., then V(t+1) chunks).  The scheduling barriers
-        // keep this order.
+        // the slot's VALU slice and at most one staging step: the K(t+2) and
+        // V(t) chunks fetched last iteration go to LDS in slots 0, 2, ..,
+        // then their registers are refilled with K(t+3) and V(t+1) in the odd
+        // slots after that.  The scheduling barriers keep this order.
 #pragma unroll
         for (int p = 0; p < kAhead; ++p) read(p);
         __builtin_amdgcn_sched_barrier(0);
+        if (C::kWaves == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int p = 0; p < C::kSlots; ++p) {
             if (p + kAhead < C::kSlots) read(p + kAhead);
             mfma(p);
             __builtin_amdgcn_sched_barrier(0);
             valu(p);
-            if (p % 2 == 1 && p / 2 < C::kStage) fetch1(stk[p / 2], rK, t + 3, p / 2);
-            if (p % 2 == 1 && p / 2 >= C::kStage && p / 2 < 2 * C::kStage)
-                fetch1(stv[p / 2 - C::kStage], rV, t + 1, p / 2 - C::kStage);
+            if (p % 2 == 0 && p / 2 < C::kStage) put_k1(kb_store, stk[p / 2], p / 2);
+            if (p % 2 == 0 && p / 2 >= C::kStage && p / 2 < 2 * C::kStage)
+                put_v1(vb_store, stv[p / 2 - C::kStage], p / 2 - C::kStage);
+            const int q = p - 2 * C::kStage - 1;
+            if (q >= 0 && q % 2 == 0 && q / 2 < C::kStage) fetch1(stk[q / 2], rK, t + 3, q / 2);
+            if (q >= 0 && q % 2 == 0 && q / 2 >= C::kStage && q / 2 < 2 * C::kStage)
+                fetch1(stv[q / 2 - C::kStage], rV, t + 1, q / 2 - C::kStage);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // The tile's weights for this row sum to at most 2^kLazy: every
         // weight is then <= 2^kLazy and the reference max stays.  Otherwise
         // (the row max moved up, or m2 was still -inf) take the recurrence
@@ -496,9 +507,10 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                   int N, float c, uint32_t q_and, uint32_t q_xor, hipStream_t stream) {
-    const int n_qtiles = (N + kBQ - 1) / kBQ;
+    using C = Cfg<D>;
+    const int n_qtiles = (N + C::kBQ - 1) / C::kBQ;
     const int n_wg = n_qtiles * BH;
-    hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                        static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
                        static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, N,
                        n_qtiles, n_wg, c, q_and, q_xor);
