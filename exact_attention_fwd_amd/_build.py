@@ -25,6 +25,11 @@ HIP_FLAGS = [
     "-fPIC",
     "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The per-tile instruction stream is one fully unrolled loop of up to 64
+    # slots (d = 256); above LLVM's default pragma-unroll size limit it would
+    # stay a loop with run-time indices into register arrays, which the
+    # compiler then moves to LDS.
+    "-mllvm", "-pragma-unroll-threshold=200000",
 ]
 
 

@@ -27,13 +27,14 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o,
                        int causal, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
-    // Per-head byte offsets are 32-bit buffer offsets: N * d * 2 plus one
-    // tile of prefetch must stay below 2^31.
+    // Per-head byte offsets are 32-bit buffer offsets: N * d * 2 plus a few
+    // tiles of prefetch must stay below 2^31.
     if (N > (1 << 22)) return FA2_ERR_INVALID_ARG;
     const int64_t rows = int64_t(B) * H * N;
     if (rows > INT32_MAX) return FA2_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA2_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+    if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED;
+    if (int64_t(N) * d > (int64_t(1) << 29)) return FA2_ERR_INVALID_ARG;
     const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                            reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
                            reinterpret_cast<uintptr_t>(lse);
@@ -66,7 +67,7 @@ extern "C" const char* fa2_status_string(int status) {
     switch (status) {
         case FA2_OK: return "ok";
         case FA2_ERR_INVALID_ARG: return "invalid argument";
-        case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
+        case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (32, 64, 96, 128 or 256 only)";
         case FA2_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case FA2_ERR_NO_DEVICE: return "no usable gfx950 device";
         case FA2_ERR_LAUNCH: return "kernel launch failed";

@@ -16,9 +16,11 @@
 // 128-bit loads, bank-spread shared tiles and row-owning warps.
 //
 //  * Each wave owns 32 whole query rows, so every row reduction stays inside
-//    the wave.  A workgroup is 8 waves (256 queries of one (batch, head), one
-//    workgroup per CU) at d = 128 and 4 waves (128 queries, two independent
-//    workgroups per CU) at d = 64; either way two waves share each SIMD.
+//    the wave.  Head dims 32, 64, 96, 128 and 256 are compiled.  A workgroup
+//    is 8 waves (256 queries of one (batch, head), one workgroup per CU) at
+//    d = 128 and 4 waves (128 queries) otherwise; two waves share each SIMD,
+//    except at d = 256, where a wave's 32x256 fp32 accumulator needs the
+//    registers of a whole SIMD.
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_f16 (A = 32 keys x 16 dims from LDS, B = Q^T held in
 //    registers for the whole loop).  In the 32x32 accumulator a lane then
@@ -103,8 +105,11 @@ constexpr int kAhead = 4;                // LDS operand reads in flight ahead of
 
 template <int D>
 struct Cfg {
-    // Waves per workgroup (see the header): 8 at d = 128, 4 at d = 64.
-    static constexpr int kWaves = D == 64 ? 4 : 8;
+    // Waves per workgroup (see the header): 8 at d = 128, 4 otherwise.  Two
+    // waves per SIMD, except at d = 256, whose registers need a SIMD each.
+    static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
+    static constexpr int kWaves = D == 128 ? 8 : 4;
+    static constexpr int kWavesPerSimd = D == 256 ? 1 : 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBQ = kWaves * kQW;               // query rows per workgroup
     static constexpr int kRowBytes = D * 2;
@@ -119,7 +124,7 @@ struct Cfg {
     // Element pairs enter the three-stage VALU chain (scaled score, exp2,
     // sum + fp16) in slots [kE0, kE1); a pair's last stage runs two slots
     // after its first.
-    static constexpr int kE0 = D == 128 ? 2 : 0;
+    static constexpr int kE0 = kDBlocks > 2 ? kDBlocks - 2 : 0;
     static constexpr int kE1 = kSlots - 2;
     static constexpr int pair_begin(int p) {
         return p <= kE0 ? 0 : p >= kE1 ? 16 : ((p - kE0) * 16) / (kE1 - kE0);
@@ -169,7 +174,7 @@ __device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(Cfg<D>::kThreads)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(Cfg<D>::kWavesPerSimd, Cfg<D>::kWavesPerSimd)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
                     float* __restrict__ LSE, int N, int n_qtiles, int n_wg, float c,
@@ -219,7 +224,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Tiles below n_full need no mask for any row of the workgroup.
     const int n_full = CAUSAL ? min(N / kBK, (q0 + 1) / kBK) : N / kBK;
 
-    // Staging: thread (wave w, lane i) moves chunks w + 8*j (j < kStage) of
+    // Staging: thread (wave w, lane i) moves chunks w + kWaves*j (j < kStage) of
     // key row i of a tile; the LDS address follows the tile's layout.
     u32x4 stk[C::kStage], stv[C::kStage];
     auto fetch1 = [&](u32x4& dst, __amdgpu_buffer_rsrc_t r, int kt, int j) {
@@ -530,12 +535,25 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
     const float c = zero ? 1.0f : static_cast<float>(a * 1.4426950408889634);
     const uint32_t q_and = zero ? 0u : 0xffffffffu;
     const uint32_t q_xor = (!zero && scale < 0.f) ? 0x80008000u : 0u;
-    if (d == 64) {
-        return causal ? launch<64, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
-                      : launch<64, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+    switch (d) {
+        case 32:
+            return causal ? launch<32, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
+                          : launch<32, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+        case 64:
+            return causal ? launch<64, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
+                          : launch<64, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+        case 96:
+            return causal ? launch<96, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
+                          : launch<96, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+        case 128:
+            return causal ? launch<128, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
+                          : launch<128, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+        case 256:
+            return causal ? launch<256, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
+                          : launch<256, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+        default:
+            return hipErrorInvalidValue;
     }
-    return causal ? launch<128, true>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream)
-                  : launch<128, false>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
 }
 
 }  // namespace fa2

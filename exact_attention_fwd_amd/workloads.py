@@ -8,7 +8,9 @@ The workloads follow the shapes the pages measure on: the pages' Triton
 comparison runs [B, H, N, d] = [4, 32, 2048, 64] in fp16 ("Implementing
 FlashAttention 1 and 2 forward in Triton", section on the reference shape),
 and the CuTe write-up covers head dims 64 and 128 with sequences up to 64K
-("FlashAttention-2 from scratch in CuTe", summary).  No public dataset is
+("FlashAttention-2 from scratch in CuTe", summary).  Head dims 32, 96 and 256
+(the Triton page's remark on head dims above 128, the CuTe write-up's notes
+on 32 and 96) run the reference shape, with 16 heads at d = 256.  No public dataset is
 involved: every tensor is i.i.d. Gaussian, drawn as float32 with numpy's
 PCG64 generator, scaled by sigma and rounded to fp16 (round-to-nearest-even).
 Draw order is Q, then K, then V from one generator seeded with ``seed``.
@@ -59,6 +61,12 @@ WORKLOADS = {
         Workload("hd128_16k", 2, 16, 16384, 128, False, 0.5, sampled_rows=512),
         Workload("long_64k", 1, 16, 65536, 128, False, 0.5, sampled_rows=512),
         Workload("long_64k_causal", 1, 16, 65536, 128, True, 0.5, sampled_rows=512),
+        # head-dim coverage: the reference shape at d = 32 and 96, and d = 256
+        # with half the heads (same bytes per tensor as d = 128)
+        Workload("hd32", 4, 32, 2048, 32, False, 1.0, sampled_rows=512),
+        Workload("hd96", 4, 32, 2048, 96, False, 1.0, sampled_rows=512),
+        Workload("hd256", 4, 16, 2048, 256, False, 1.0, sampled_rows=512),
+        Workload("hd256_causal", 4, 16, 2048, 256, True, 1.0, sampled_rows=512),
     ]
 }
 

@@ -32,7 +32,7 @@ typedef enum {
     FA2_OK = 0,
     FA2_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, grid too large,
                                 non-finite scale, output aliasing an input     */
-    FA2_ERR_UNSUPPORTED = 2, /* head dim other than 64 or 128                  */
+    FA2_ERR_UNSUPPORTED = 2, /* head dim not one of 32, 64, 96, 128, 256       */
     FA2_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned                  */
     FA2_ERR_NO_DEVICE = 4,   /* no usable gfx950 device / HIP runtime failure  */
     FA2_ERR_LAUNCH = 5       /* the kernel launch failed                       */
@@ -49,8 +49,8 @@ typedef enum {
  *             log-sum-exp of the scaled scores of each query row over its
  *             visible keys.
  *   B, H, N : batch, heads, sequence length (queries = keys = N); each >= 1,
- *             N <= 4194304 (2^22) and B * H * N <= 2^31 - 1.
- *   d       : head dimension, 64 or 128.
+ *             N <= 4194304 (2^22), N * d <= 2^29 and B * H * N <= 2^31 - 1.
+ *   d       : head dimension: 32, 64, 96, 128 or 256.
  *   scale   : softmax scale (normally 1/sqrt(d)); any finite value.  0 gives
  *             uniform weights over the visible keys.
  *   causal  : non-zero: query i sees keys j <= i only (top-left aligned).

@@ -79,9 +79,19 @@ def test_non_finite_scale(lib, scale):
     assert call(scale=scale) == fa2.FA2_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("d", [0, 32, 63, 96, 256])
+@pytest.mark.parametrize("d", [0, 16, 48, 63, 80, 160, 192, 512])
 def test_unsupported_head_dim(lib, d):
     assert call(d=d) == fa2.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_sequence_length_limit_per_head_dim(lib, d):
+    # N * d * 2 bytes per head must fit the 32-bit buffer offsets: N * d <=
+    # 2^29 (and N <= 2^22).  A misaligned Q, checked after the length rule,
+    # shows which lengths pass it without reaching a HIP call.
+    n_max = min(1 << 22, (1 << 29) // d)
+    assert call(q=Q + 2, N=n_max, d=d) == fa2.FA2_ERR_MISALIGNED
+    assert call(q=Q + 2, N=n_max + 1, d=d) == fa2.FA2_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])

@@ -3,10 +3,11 @@ same seeded inputs, through the C ABI (python binding -> libfa2.so).
 
 Workloads: the five configurations of the pages' shapes (tiny, [4,32,2048,64]
 non-causal and causal, [2,16,16384,128], [1,16,65536,128] non-causal and
-causal) plus [4,32,2048,128]; large ones are checked on 512 seeded query rows
+causal) plus [4,32,2048,128] and the head-dim cases [4,32,2048,32],
+[4,32,2048,96], [4,16,2048,256] (also causal); large ones are checked on 512 seeded query rows
 per (batch, head) and, for every element, on properties that hold at any
 size (finiteness, closed forms).  Edge cases: the pages' worked example
-embedded in d = 64, odd N (tails), stress inputs that move the running max,
+embedded in d = 64, odd N (tails) at every head dim, stress inputs that move the running max,
 scale 0 / negative, determinism, NaN-poisoned and guard-banded outputs.
 """
 import functools
@@ -20,6 +21,8 @@ from oracle import attention_fp64
 from parity import diff, run_gpu, say
 
 pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = [32, 64, 96, 128, 256]
 
 torch = pytest.importorskip("torch")
 
@@ -60,7 +63,8 @@ def test_tiny_causal():
     check("tiny_causal", q, k, v, w.scale, True)
 
 
-@pytest.mark.parametrize("name", ["ref_d128", "hd128_16k", "long_64k", "long_64k_causal"])
+@pytest.mark.parametrize("name", ["ref_d128", "hd128_16k", "long_64k", "long_64k_causal",
+                                  "hd32", "hd96", "hd256", "hd256_causal"])
 def test_workload_sampled(name):
     w = WORKLOADS[name]
     q, k, v = inputs(w.B, w.H, w.N, w.d, w.sigma, w.seed)
@@ -105,7 +109,7 @@ def test_exercise2_constant_values_in_d64():
 
 
 # -------------------------------------------------------------- tails, odd N
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n", [1, 4, 17, 63, 65, 129, 1000])
 def test_odd_lengths(n, d, causal):
@@ -113,7 +117,7 @@ def test_odd_lengths(n, d, causal):
     check(f"N={n} d={d} causal={causal}", q, k, v, d ** -0.5, causal)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", HEAD_DIMS)
 def test_batch_heads_and_ragged_tail_together(d):
     q, k, v = make_qkv(3, 5, 300, d, 1.0, seed=7)
     for causal in (False, True):
@@ -122,7 +126,7 @@ def test_batch_heads_and_ragged_tail_together(d):
 
 # ----------------------------------------------------------- stress inputs
 @pytest.mark.parametrize("kind", ["rising", "falling", "large", "const_v", "zero_q"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("causal", [False, True])
 def test_stress(kind, d, causal):
     q, k, v = stress_inputs(kind, 1, 2, 333, d, seed=3)
@@ -206,7 +210,7 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("jump", [3.0, 20.0])
 def test_row_max_jumps_mid_sequence(d, causal, jump):
