@@ -1,4 +1,4 @@
-"""CPU oracle for the FlashAttention-2 forward pass.
+"""CPU oracle for the FlashAttention-2 forward pass and its gradients.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this package: it is used by ``tests/``, by the ``cpu_baseline`` leg of
@@ -8,8 +8,8 @@ two meet only in the seeded input generators, which hold none of the method's
 arithmetic.
 
 Everything here is plain float64 numpy (plus one pure-Python brute force for
-tiny cases).  See ``oracle.attention`` for the functions and the passages of
-the pages each one follows.
+tiny cases).  See ``oracle.attention`` (forward) and ``oracle.attention_bwd``
+(gradients) for the functions and the passages of the pages each one follows.
 """
 from .attention import (
     attention_fp64,
@@ -17,10 +17,12 @@ from .attention import (
     online_softmax_attention,
     brute_force_attention,
 )
+from .attention_bwd import attention_bwd_fp64
 
 __all__ = [
     "attention_fp64",
     "attention_probs_fp64",
     "online_softmax_attention",
     "brute_force_attention",
+    "attention_bwd_fp64",
 ]
