@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the FlashAttention-2 forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ref]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ref] [--pass fwd|bwd]
 
 Without --warmup / --steps, W fills about 0.4 s and K about 0.25 s of
 launches (the GPU's clock needs ~0.1 s of load to settle; a short kernel
@@ -22,6 +22,12 @@ roofline   the kernel's average launch time from HIP events on the stream it
            since they were taken);
 cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded
            sample of the same workload (a reported baseline, not a target).
+
+--pass bwd times the backward pass instead: a step is one fa2_bwd call (the
+dQ kernel, then the dK/dV kernel) on the forward's O and LSE and a seeded
+upstream gradient; FLOPs = 10*B*H*N^2*d (five products of 2*N^2*d: S, dP,
+dV, dK, dQ; halved when causal), the roofline unit is the whole call, and
+the CPU baseline is the float64 gradient oracle.
 """
 from __future__ import annotations
 
@@ -38,9 +44,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FA2 fwd TFLOP/s and % of MI355X fp16 MFMA peak, [4,32,2048,64]"
+METRIC_BWD = "FA2 bwd TFLOP/s and % of MI355X fp16 MFMA peak"
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_fwd_amd", "csrc", f)
-                  for f in ("fa2_fwd_gfx950.hip", "fa2_api.cpp", "fa2_launch.h")]
+                  for f in ("fa2_fwd_gfx950.hip", "fa2_bwd_gfx950.hip", "fa2_device.h", "fa2_api.cpp",
+                            "fa2_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -105,12 +113,48 @@ def cpu_baseline(w, q, k, v, budget_s: float):
             "sample": sample, "seconds": round(dt, 3)}
 
 
+def bwd_flops(w) -> float:
+    """10*B*H*N^2*d: S = Q K^T, dP = dO V^T, dV = P^T dO, dK = dS^T Q and
+    dQ = dS K, 2*N^2*d each per head; halved when causal."""
+    f = 10.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if w.causal else f
+
+
+def upstream_grad(w):
+    """The seeded upstream gradient dO of a workload, N(0, 1) in fp16."""
+    from exact_attention_fwd_amd.workloads import make_qkv
+    return make_qkv(w.B, w.H, w.N, w.d, 1.0, w.seed + 7919)[0]
+
+
+def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
+    """Time the gradient oracle on whole heads, as many as fit ~budget_s."""
+    from oracle import attention_bwd_fp64
+    from oracle.attention import oracle_threads
+
+    threads = oracle_threads()
+    t0 = time.perf_counter()
+    attention_bwd_fp64(q[:1, :1], k[:1, :1], v[:1, :1], do[:1, :1], w.scale, causal=w.causal,
+                       threads=1)
+    one = max(time.perf_counter() - t0, 1e-4)
+    n_heads = max(1, int(min(w.B * w.H, max(threads, budget_s * threads / one))))
+    sl = (x.reshape(1, w.B * w.H, w.N, w.d)[:, :n_heads] for x in (q, k, v, do))
+    t0 = time.perf_counter()
+    attention_bwd_fp64(*sl, w.scale, causal=w.causal, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = n_heads * bwd_flops(w) / (w.B * w.H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_heads} of {w.B * w.H} heads of {w.name}, all gradients",
+            "seconds": round(dt, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: ~0.25 s worth)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: ~0.4 s worth)")
     ap.add_argument("--workload", default="ref")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward pass")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -153,13 +197,23 @@ def main():
     # One validated call through the torch wrapper, then the timed steps call
     # the C entry point itself with the same (cached) pointers and stream.
     fa2.fwd(tq, tk, tv, scale=w.scale, causal=w.causal, out=out, lse=lse)
-    args_c = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
-              w.B, w.H, w.N, w.d, w.scale, w.causal, stream.cuda_stream)
+    if args.which == "fwd":
+        entry = fa2.fa2_fwd
+        args_c = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  w.B, w.H, w.N, w.d, w.scale, w.causal, stream.cuda_stream)
+    else:
+        do = upstream_grad(w)
+        tdo = torch.from_numpy(do).to(dev)
+        gq, gk, gv, gdelta = fa2.bwd(tq, tk, tv, out, lse, tdo, scale=w.scale, causal=w.causal)
+        entry = fa2.fa2_bwd
+        args_c = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  tdo.data_ptr(), gq.data_ptr(), gk.data_ptr(), gv.data_ptr(), gdelta.data_ptr(),
+                  w.B, w.H, w.N, w.d, w.scale, w.causal, stream.cuda_stream)
 
     def step():
-        status = fa2.fa2_fwd(*args_c)
+        status = entry(*args_c)
         if status != fa2.FA2_OK:
-            raise RuntimeError(f"fa2_fwd: {fa2.fa2_status_string(status)}")
+            raise RuntimeError(f"{args.which}: {fa2.fa2_status_string(status)}")
 
     # Size the default warm-up and timed loop from a few probe launches (they
     # count as warm-up).
@@ -191,7 +245,7 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
-    flops = w.flops()
+    flops = w.flops() if args.which == "fwd" else bwd_flops(w)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
@@ -199,7 +253,7 @@ def main():
         f"{value:.1f} TFLOP/s ({100 * value / PEAK_FP16_TFLOPS:.1f}% of peak)")
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -218,11 +272,30 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(w.name if args.which == "fwd" else f"bwd:{w.name}"),
                      "launch_ms": round(ev_ms, 5)},
     }
 
-    if not args.no_parity:
+    if args.which == "bwd":
+        result["config"]["pass"] = "backward (dQ, dK, dV, delta)"
+    if not args.no_parity and args.which == "bwd":
+        # the first two heads of the timed output, every element, in units of
+        # each gradient's rounding-error bound u (|G| + E + 2^-14)
+        from oracle import attention_bwd_fp64
+        from oracle.attention_bwd import attention_bwd_error_scale
+        nh = min(2, w.B * w.H)
+        sl = [x.reshape(1, w.B * w.H, w.N, w.d)[:, :nh] for x in (q, k, v, do)]
+        ref = attention_bwd_fp64(*sl, w.scale, causal=w.causal)
+        esc = attention_bwd_error_scale(*sl, w.scale, causal=w.causal)
+        got = [t.reshape(1, w.B * w.H, *t.shape[2:])[:, :nh].cpu().numpy().astype(np.float64)
+               for t in (gq, gk, gv, gdelta)]
+        u = 2.0 ** -11
+        ratios = {name: float((np.abs(g - r) / (u * (np.abs(r) + e + 2.0 ** -14))).max())
+                  for name, g, r, e in zip(("dq", "dk", "dv", "delta"), got, ref, esc)}
+        result["parity"] = {"heads": nh, "max_ratio_to_rounding_bound": ratios,
+                            "pass": bool(max(ratios.values()) <= 2.0)}
+        log(f"[bench] parity {result['parity']}")
+    elif not args.no_parity:
         # sampled parity of the timed output, 64 seeded rows per (b, h)
         from oracle import attention_fp64
         rows = np.stack([np.stack([sample_rows(w.N, b, h, 64) for h in range(w.H)])
@@ -243,7 +316,8 @@ def main():
         result["cpu_baseline"] = None
     else:
         log("[bench] timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        result["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_budget) if args.which == "fwd"
+                                  else cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget))
         log(f"[bench] cpu baseline {result['cpu_baseline']}")
 
     print(json.dumps(result), flush=True)

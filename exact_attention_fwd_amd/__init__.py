@@ -1,8 +1,9 @@
-"""FlashAttention-2 forward pass for AMD MI355X (gfx950).
+"""FlashAttention-2 forward pass (and its backward) for AMD MI355X (gfx950).
 
 ``fwd(q, k, v, scale=None, causal=False) -> (o, lse)`` runs the library's
-hand-written gfx950 kernels on torch fp16 tensors; ``fa2_fwd`` is the C entry
-point itself (raw device addresses).  The seeded synthetic workloads live in
+hand-written gfx950 kernels on torch fp16 tensors, ``bwd(q, k, v, o, lse,
+dout, ...) -> (dq, dk, dv, delta)`` their gradients; ``fa2_fwd`` and
+``fa2_bwd`` are the C entry points themselves (raw device addresses).  The seeded synthetic workloads live in
 ``exact_attention_fwd_amd.workloads``.
 """
 from ._lib import (  # noqa: F401
@@ -15,6 +16,8 @@ from ._lib import (  # noqa: F401
     FA2_OK,
     LIB_PATH,
     Fa2Error,
+    bwd,
+    fa2_bwd,
     fa2_fwd,
     fa2_last_hip_error,
     fa2_status_string,

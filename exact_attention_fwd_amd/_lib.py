@@ -1,7 +1,7 @@
 """ctypes binding of libfa2.so (include/fa2.h): argument marshalling only.
 
-Every step of the attention forward pass runs in the library's gfx950
-kernels.  There is no fallback: if the library is missing or does not load,
+Every step of the attention forward and backward passes runs in the
+library's gfx950 kernels.  There is no fallback: if the library is missing or does not load,
 the first call raises.
 """
 from __future__ import annotations
@@ -19,14 +19,14 @@ FA2_ERR_MISALIGNED = 3
 FA2_ERR_NO_DEVICE = 4
 FA2_ERR_LAUNCH = 5
 
-EXPORTED = ("fa2_fwd", "fa2_status_string", "fa2_last_hip_error", "fa2_version")
+EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_status_string", "fa2_last_hip_error", "fa2_version")
 
 _lock = threading.Lock()
 _lib = None
 
 
 class Fa2Error(RuntimeError):
-    """A non-zero status from fa2_fwd."""
+    """A non-zero status from fa2_fwd or fa2_bwd."""
 
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -47,6 +47,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.fa2_fwd.restype = ctypes.c_int
+        lib.fa2_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa2_bwd.restype = ctypes.c_int
         lib.fa2_status_string.argtypes = [ctypes.c_int]
         lib.fa2_status_string.restype = ctypes.c_char_p
         lib.fa2_last_hip_error.argtypes = []
@@ -65,6 +68,12 @@ def fa2_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
                                   float(scale), int(bool(causal)), stream)
 
 
+def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> int:
+    """The C entry point, same arguments (device addresses as ints)."""
+    return load_library().fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H),
+                                  int(N), int(d), float(scale), int(bool(causal)), stream)
+
+
 def fa2_status_string(status: int) -> str:
     return load_library().fa2_status_string(int(status)).decode()
 
@@ -77,6 +86,34 @@ def fa2_version() -> str:
     return load_library().fa2_version().decode()
 
 
+def _check_qkv(named):
+    import torch
+
+    first = named[0][1]
+    for name, t in named:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor")
+        if t.dtype != torch.float16:
+            raise ValueError(f"{name} must be float16")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+        if t.shape != first.shape:
+            raise ValueError(f"{name} must have the shape of {named[0][0]}")
+        if t.device != first.device:
+            raise ValueError(f"{name} must be on the device of {named[0][0]}")
+
+
+def _out(t, like, dtype, shape, name):
+    import torch
+
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() \
+            or t.device != like.device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t
+
+
 def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """O, LSE = attention forward of torch fp16 CUDA tensors [B, H, N, d].
 
@@ -87,30 +124,12 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise ValueError(f"{name} must be a CUDA tensor")
-        if t.dtype != torch.float16:
-            raise ValueError(f"{name} must be float16")
-        if t.dim() != 4 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
-    if q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k and v must have the same shape")
-    if q.device != k.device or q.device != v.device:
-        raise ValueError("q, k and v must be on one device")
+    _check_qkv((("q", q), ("k", k), ("v", v)))
     B, H, N, d = q.shape
     if scale is None:
         scale = d ** -0.5
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() \
-            or out.device != q.device:
-        raise ValueError("out must be a contiguous fp16 tensor shaped like q")
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
-            or lse.device != q.device:
-        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    out = _out(out, q, torch.float16, q.shape, "out")
+    lse = _out(lse, q, torch.float32, (B, H, N), "lse")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     status = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -119,3 +138,35 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
         raise Fa2Error(status, f"fa2_fwd failed: {fa2_status_string(status)} "
                                f"(hip error {fa2_last_hip_error()})")
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None,
+        delta=None, stream=None):
+    """dQ, dK, dV (and delta) of the attention forward, on torch tensors.
+
+    q, k, v, o, dout are fp16 CUDA tensors [B, H, N, d] (o and lse the
+    forward's outputs for the same arguments), lse fp32 [B, H, N].  Output
+    buffers may be passed to reuse memory; ``delta`` (fp32 [B, H, N]) is the
+    workspace the library fills with dO . O per row.  ``scale`` defaults to
+    1/sqrt(d).  Returns (dq, dk, dv, delta).
+    """
+    import torch
+
+    _check_qkv((("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)))
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    lse = _out(lse, q, torch.float32, (B, H, N), "lse")
+    dq = _out(dq, q, torch.float16, q.shape, "dq")
+    dk = _out(dk, q, torch.float16, q.shape, "dk")
+    dv = _out(dv, q, torch.float16, q.shape, "dv")
+    delta = _out(delta, q, torch.float32, (B, H, N), "delta")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                     delta.data_ptr(), B, H, N, d, scale, causal, stream)
+    if status != FA2_OK:
+        raise Fa2Error(status, f"fa2_bwd failed: {fa2_status_string(status)} "
+                               f"(hip error {fa2_last_hip_error()})")
+    return dq, dk, dv, delta

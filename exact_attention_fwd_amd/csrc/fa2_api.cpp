@@ -20,35 +20,21 @@ bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
     return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
-}  // namespace
-
-extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o,
-                       float* lse, int B, int H, int N, int d, float scale,
-                       int causal, void* stream) {
-    if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+// Sizes, scale and head dim shared by both entry points; 0 when valid.
+int check_sizes(int B, int H, int N, int d, float scale, int max_d) {
     if (B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
     // Per-head byte offsets are 32-bit buffer offsets: N * d * 2 plus a few
     // tiles of prefetch must stay below 2^31.
     if (N > (1 << 22)) return FA2_ERR_INVALID_ARG;
-    const int64_t rows = int64_t(B) * H * N;
-    if (rows > INT32_MAX) return FA2_ERR_INVALID_ARG;
+    if (int64_t(B) * H * N > INT32_MAX) return FA2_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA2_ERR_INVALID_ARG;
-    if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA2_ERR_UNSUPPORTED;
+    if ((d != 32 && d != 64 && d != 96 && d != 128 && d != 256) || d > max_d)
+        return FA2_ERR_UNSUPPORTED;
     if (int64_t(N) * d > (int64_t(1) << 29)) return FA2_ERR_INVALID_ARG;
-    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
-                           reinterpret_cast<uintptr_t>(lse);
-    if (bits & 15u) return FA2_ERR_MISALIGNED;
-    const size_t t_bytes = size_t(rows) * size_t(d) * 2;
-    const size_t l_bytes = size_t(rows) * 4;
-    for (const void* in : {q, k, v}) {
-        if (overlaps(o, t_bytes, in, t_bytes) || overlaps(lse, l_bytes, in, t_bytes))
-            return FA2_ERR_INVALID_ARG;
-    }
-    if (overlaps(lse, l_bytes, o, t_bytes)) return FA2_ERR_INVALID_ARG;
+    return 0;
+}
 
-    const hipError_t err = fa2::launch_fwd(q, k, v, o, lse, B * H, N, d, scale, causal != 0,
-                                           static_cast<hipStream_t>(stream));
+int launch_status(hipError_t err) {
     if (err == hipSuccess) return FA2_OK;
     g_last_hip_error = static_cast<int>(err);
     switch (err) {
@@ -63,11 +49,66 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o,
     }
 }
 
+}  // namespace
+
+extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int H, int N, int d, float scale,
+                       int causal, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+    if (const int st = check_sizes(B, H, N, d, scale, /*max_d=*/256)) return st;
+    const int64_t rows = int64_t(B) * H * N;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(lse);
+    if (bits & 15u) return FA2_ERR_MISALIGNED;
+    const size_t t_bytes = size_t(rows) * size_t(d) * 2;
+    const size_t l_bytes = size_t(rows) * 4;
+    for (const void* in : {q, k, v}) {
+        if (overlaps(o, t_bytes, in, t_bytes) || overlaps(lse, l_bytes, in, t_bytes))
+            return FA2_ERR_INVALID_ARG;
+    }
+    if (overlaps(lse, l_bytes, o, t_bytes)) return FA2_ERR_INVALID_ARG;
+
+    return launch_status(fa2::launch_fwd(q, k, v, o, lse, B * H, N, d, scale, causal != 0,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       float* delta, int B, int H, int N, int d, float scale, int causal,
+                       void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
+        return FA2_ERR_INVALID_ARG;
+    if (const int st = check_sizes(B, H, N, d, scale, /*max_d=*/128)) return st;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(dout) |
+                           reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) |
+                           reinterpret_cast<uintptr_t>(dv) | reinterpret_cast<uintptr_t>(delta);
+    if (bits & 15u) return FA2_ERR_MISALIGNED;
+    const size_t rows = size_t(B) * H * N;
+    const size_t t_bytes = rows * size_t(d) * 2;
+    const size_t l_bytes = rows * 4;
+    const struct { const void* p; size_t n; } ins[] = {
+        {q, t_bytes}, {k, t_bytes}, {v, t_bytes}, {o, t_bytes}, {lse, l_bytes}, {dout, t_bytes}};
+    const struct { const void* p; size_t n; } outs[] = {
+        {dq, t_bytes}, {dk, t_bytes}, {dv, t_bytes}, {delta, l_bytes}};
+    for (const auto& w : outs) {
+        for (const auto& r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA2_ERR_INVALID_ARG;
+        for (const auto& w2 : outs)
+            if (&w2 != &w && overlaps(w.p, w.n, w2.p, w2.n)) return FA2_ERR_INVALID_ARG;
+    }
+    return launch_status(fa2::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B * H, N, d,
+                                         scale, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char* fa2_status_string(int status) {
     switch (status) {
         case FA2_OK: return "ok";
         case FA2_ERR_INVALID_ARG: return "invalid argument";
-        case FA2_ERR_UNSUPPORTED: return "unsupported head dimension (32, 64, 96, 128 or 256 only)";
+        case FA2_ERR_UNSUPPORTED:
+            return "unsupported head dimension (forward: 32, 64, 96, 128, 256; backward: 32 to 128)";
         case FA2_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case FA2_ERR_NO_DEVICE: return "no usable gfx950 device";
         case FA2_ERR_LAUNCH: return "kernel launch failed";

@@ -1,0 +1,428 @@
+// Backward pass of the attention forward for AMD MI355X (gfx950 / CDNA4).
+//
+// What is computed.  For the forward O = softmax(sigma Q K^T) V of one
+// (batch, head), with causal masking when asked, and an upstream gradient
+// dO, the gradients of <dO, O>:
+//     P  = exp(sigma S - LSE)            S = Q K^T, LSE the forward's statistic
+//     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),   delta_i = dO_i . O_i
+//     dQ = sigma dS K,   dK = sigma dS^T Q.
+// The N x N matrices S, P, dP, dS are never stored: every tile recomputes S
+// and P from Q, K and the per-row LSE the forward kept ("3.6 Attention I --
+// the memory problem and FlashAttention principles", 3.6.7: recompute instead
+// of store, with only O(N) row statistics kept).  The formulas are the chain
+// rule through the row softmax; delta_i equals sum_k P_ik dP_ik because
+// O_i = sum_k P_ik V_k.
+//
+// Two kernels, no atomics, deterministic:
+//  * dQ kernel -- grid over (query tile, batch*head) like the forward; each
+//    wave owns 32 queries, holds Q^T and dO^T of them as MFMA B operands,
+//    computes delta_i once (and writes it for the second kernel), then loops
+//    over key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T in registers,
+//    dQ^T += K^T dS^T with K^T read from LDS through ds_read_b64_tr_b16.
+//  * dK/dV kernel -- grid over (key tile, batch*head); each wave owns 32
+//    keys, holds K^T and V^T of them, and loops over query tiles:
+//    S = Q K^T, dP = dO V^T, P and dS in registers, dV^T += dO^T P and
+//    dK^T += Q^T dS with Q^T and dO^T read transposed from LDS.
+//  In both, an accumulator's register order is the B operand of the next
+//  product (fa2_device.h), so P and dS never leave registers.
+//  Tiles of 64 rows are double-buffered in LDS through registers (the next
+//  tile's loads are issued before the current tile's products), one barrier
+//  per tile.  Causal work stops at the diagonal; the tiles that cross it are
+//  masked.  Rows past N read as zero through the per-head buffer resources,
+//  which makes their contributions exactly zero, and their stores are
+//  dropped.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "fa2_device.h"
+#include "fa2_launch.h"
+
+namespace fa2 {
+namespace {
+
+using namespace dev;
+
+template <int D>
+struct BwdCfg {
+    static_assert(D == 32 || D == 64 || D == 96 || D == 128, "head dim");
+    static constexpr int kWaves = 4;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kRows = kWaves * kQW;         // queries (dQ) or keys (dK, dV) per workgroup
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+    static constexpr int kTileBytes = kBK * kRowBytes;
+    static constexpr int kDSteps = D / 16;             // k-steps over the head dim
+    static constexpr int kDBlocks = D / 32;            // 32-row blocks of a transposed accumulator
+    static constexpr int kStage = kChunks / kWaves;    // staged chunks per thread per tensor and tile
+    // The dK/dV kernel keeps K^T, V^T and two accumulators of D x 32 per
+    // wave: at D = 128 that needs the registers of a whole SIMD.
+    static constexpr int kWavesPerSimdQ = 2;
+    static constexpr int kWavesPerSimdKV = D >= 128 ? 1 : 2;
+};
+
+__device__ __forceinline__ f32x16 mfma(const h8& a, const h8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Per-lane bases of the plain A-operand reads (32 rows x 16 head-dim
+// columns: row 32*blk + l32, chunk 2*ds + hi) from a swizzled tile.  The
+// chunk's low bits are 2*(ds&1) + hi, so two bases cover every (ds, blk):
+// the rest is the compile-time offset sw_imm(ds, blk).
+struct SwBase {
+    int b[2];
+    __device__ __forceinline__ explicit SwBase(int lane) {
+        const int l32 = lane & 31, hi = lane >> 5;
+        b[0] = (hi * 64 + (l32 ^ (4 * hi))) << 4;
+        b[1] = (hi * 64 + (l32 ^ (8 + 4 * hi))) << 4;
+    }
+};
+__device__ __forceinline__ constexpr int sw_imm(int ds, int blk) { return (2 * ds * 64 + 32 * blk) << 4; }
+
+// Stores a 32 x D transposed accumulator (rows of this lane = row `row`,
+// columns 32*db + 8*(r/4) + 4*hi + r%4) as fp16 (RNE) after scaling by `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t r, int row, int hi,
+                                           const f32x16 (&acc)[D / 32], float mul) {
+    const int base = row * D * 2 + 8 * hi;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            h4 out;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) out[k] = (_Float16)(acc[db][4 * rr + k] * mul);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), r,
+                                                  base + 64 * db + 16 * rr, 0, 0);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdCfg<D>::kThreads)
+__attribute__((amdgpu_waves_per_eu(BwdCfg<D>::kWavesPerSimdQ, BwdCfg<D>::kWavesPerSimdQ)))
+void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                       const _Float16* __restrict__ V, const _Float16* __restrict__ O,
+                       const _Float16* __restrict__ dO, const float* __restrict__ LSE,
+                       _Float16* __restrict__ dQ, float* __restrict__ Delta, int N,
+                       int n_qtiles, int n_wg, float c2, float sigma) {
+    using C = BwdCfg<D>;
+    // K tile swizzled (plain reads for S^T, transposed reads for dQ^T), V
+    // tile chunk-major (plain reads for dP^T).
+    __shared__ __attribute__((aligned(16))) unsigned char kb0[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char kb1[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char vb0[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char vb1[C::kTileBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int logical = xcd_logical_id(blockIdx.x, n_wg);
+    const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
+    int qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
+    if (CAUSAL) qt = n_qtiles - 1 - qt;   // longest rows first
+    const int q0 = qt * C::kRows;
+    const size_t head = size_t(bh) * size_t(N) * D;
+    const uint32_t head_bytes = uint32_t(N) * C::kRowBytes;
+    const auto rQ = make_rsrc(Q + head, head_bytes);
+    const auto rK = make_rsrc(K + head, head_bytes);
+    const auto rV = make_rsrc(V + head, head_bytes);
+    const auto rO = make_rsrc(O + head, head_bytes);
+    const auto rdO = make_rsrc(dO + head, head_bytes);
+    const auto rL = make_rsrc(LSE + size_t(bh) * N, uint32_t(N) * 4);
+    const int my_q = q0 + wave * kQW + l32;
+
+    // Q^T and dO^T fragments (B operands: lane = query my_q, dims
+    // 16*ds + 8*hi + [0, 8)), and delta = dO . O of the query (the fp16
+    // products are exact in fp32; the lane pair holds the two halves).
+    h8 qf[C::kDSteps], dof[C::kDSteps];
+    float dsum = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < C::kDSteps; ++ds) {
+        const int off = my_q * C::kRowBytes + 32 * ds + 16 * hi;
+        qf[ds] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0));
+        dof[ds] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, 0, 0));
+        const h8 of = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rO, off, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsum = __builtin_fmaf((float)dof[ds][i], (float)of[i], dsum);
+    }
+    const float delta = pair_sum(dsum);
+    const float lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, my_q * 4, 0, 0)) * kLog2e;
+    if (hi == 0 && my_q < N) Delta[size_t(bh) * N + my_q] = delta;
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::kRows) : N;
+    const int n_kt = (kv_end + kBK - 1) / kBK;
+    // Tiles below n_full need no mask for any query of the workgroup.
+    const int n_full = CAUSAL ? min(N / kBK, (q0 + 1) / kBK) : N / kBK;
+
+    // Staging: thread (wave w, lane i) moves chunks w + kWaves*j of row i.
+    u32x4 stk[C::kStage], stv[C::kStage];
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            const int off = (kt * kBK + lane) * C::kRowBytes + (wave + C::kWaves * j) * 16;
+            stk[j] = __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0);
+            stv[j] = __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0);
+        }
+    };
+    auto put = [&](unsigned char* kb, unsigned char* vb) {
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            const int ch = wave + C::kWaves * j;
+            *reinterpret_cast<u32x4*>(kb + lds_v_off(ch, lane)) = stk[j];
+            *reinterpret_cast<u32x4*>(vb + lds_k_off(ch, lane)) = stv[j];
+        }
+    };
+    const SwBase ksw(lane);
+    const TrBase ktr(lane);
+    const int v_base = lds_k_off(hi, l32);
+
+    f32x16 acc[C::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) acc[db] = f32x16{};
+
+    fetch(0);
+    put(kb0, vb0);
+    __syncthreads();
+    for (int t = 0; t < n_kt; ++t) {
+        const unsigned char* kb = (t & 1) ? kb1 : kb0;
+        const unsigned char* vb = (t & 1) ? vb1 : vb0;
+        const bool more = t + 1 < n_kt;
+        if (more) fetch(t + 1);
+        const bool masked = t >= n_full;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {   // 32 keys at a time
+            f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < C::kDSteps; ++ds) {
+                const h8 ak = *reinterpret_cast<const h8*>(kb + ksw.b[ds & 1] + sw_imm(ds, blk));
+                st = mfma(ak, qf[ds], st);
+                const h8 av = *reinterpret_cast<const h8*>(vb + v_base + lds_k_off(2 * ds, 32 * blk));
+                dpt = mfma(av, dof[ds], dpt);
+            }
+            // Register r of this lane: key t*64 + 32*blk + 8*(r/4) + 4*hi + r%4.
+            h8 dsf[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -lse2));
+                if (masked) {
+                    const int key = t * kBK + 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
+                }
+                dsf[r >> 3][r & 7] = (_Float16)(p * (dpt[r] - delta));
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int db = 0; db < C::kDBlocks; ++db)
+                    acc[db] = mfma(read_tr_operand(kb, ktr, tr_imm(2 * blk + kk, db)), dsf[kk], acc[db]);
+            }
+        }
+        if (more) put((t & 1) ? kb0 : kb1, (t & 1) ? vb0 : vb1);
+        __syncthreads();
+    }
+    store_rows<D>(make_rsrc(dQ + head, head_bytes), my_q, hi, acc, sigma);
+}
+
+// -------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdCfg<D>::kThreads)
+__attribute__((amdgpu_waves_per_eu(BwdCfg<D>::kWavesPerSimdKV, BwdCfg<D>::kWavesPerSimdKV)))
+void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                         const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
+                         const float* __restrict__ LSE, const float* __restrict__ Delta,
+                         _Float16* __restrict__ dK, _Float16* __restrict__ dV, int N,
+                         int n_ktiles, int n_wg, float c2, float sigma) {
+    using C = BwdCfg<D>;
+    // Q and dO tiles swizzled (plain reads for S and dP, transposed reads for
+    // dK^T and dV^T); per-query log2-domain LSE and delta beside them.
+    __shared__ __attribute__((aligned(16))) unsigned char qb0[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char qb1[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char ob0[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char ob1[C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) float lb0[kBK], lb1[kBK], db0[kBK], db1[kBK];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int logical = xcd_logical_id(blockIdx.x, n_wg);
+    const int bh = __builtin_amdgcn_readfirstlane(logical / n_ktiles);
+    const int kt = __builtin_amdgcn_readfirstlane(logical - bh * n_ktiles);   // causal: tile 0 is the longest
+    const int k0 = kt * C::kRows;
+    const size_t head = size_t(bh) * size_t(N) * D;
+    const uint32_t head_bytes = uint32_t(N) * C::kRowBytes;
+    const auto rQ = make_rsrc(Q + head, head_bytes);
+    const auto rK = make_rsrc(K + head, head_bytes);
+    const auto rV = make_rsrc(V + head, head_bytes);
+    const auto rdO = make_rsrc(dO + head, head_bytes);
+    const auto rL = make_rsrc(LSE + size_t(bh) * N, uint32_t(N) * 4);
+    const auto rD = make_rsrc(Delta + size_t(bh) * N, uint32_t(N) * 4);
+    const int my_k = k0 + wave * kQW + l32;
+
+    // K^T and V^T fragments (B operands: lane = key my_k, dims 16*ds + 8*hi + [0, 8)).
+    h8 kf[C::kDSteps], vf[C::kDSteps];
+#pragma unroll
+    for (int ds = 0; ds < C::kDSteps; ++ds) {
+        const int off = my_k * C::kRowBytes + 32 * ds + 16 * hi;
+        kf[ds] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0));
+        vf[ds] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0));
+    }
+
+    const int n_qt = (N + kBK - 1) / kBK;
+    // Causal: queries before k0 see none of these keys; the query tiles that
+    // overlap [k0, k0 + kRows) cross the diagonal and are masked.
+    const int t0 = CAUSAL ? k0 / kBK : 0;
+    const int t_mask_end = CAUSAL ? t0 + C::kRows / kBK : 0;
+
+    u32x4 sq[C::kStage], so[C::kStage];
+    float sl = 0.f, sd = 0.f;
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            const int off = (t * kBK + lane) * C::kRowBytes + (wave + C::kWaves * j) * 16;
+            sq[j] = __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0);
+            so[j] = __builtin_amdgcn_raw_buffer_load_b128(rdO, off, 0, 0);
+        }
+        if (wave == 0) sl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (t * kBK + lane) * 4, 0, 0)) * kLog2e;
+        if (wave == 1) sd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (t * kBK + lane) * 4, 0, 0));
+    };
+    auto put = [&](unsigned char* qb, unsigned char* ob, float* lb, float* dbuf) {
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            const int ch = wave + C::kWaves * j;
+            *reinterpret_cast<u32x4*>(qb + lds_v_off(ch, lane)) = sq[j];
+            *reinterpret_cast<u32x4*>(ob + lds_v_off(ch, lane)) = so[j];
+        }
+        if (wave == 0) lb[lane] = sl;
+        if (wave == 1) dbuf[lane] = sd;
+    };
+    const SwBase sw(lane);
+    const TrBase tr(lane);
+
+    f32x16 dk[C::kDBlocks], dv[C::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    fetch(t0);
+    put(qb0, ob0, lb0, db0);
+    __syncthreads();
+    for (int t = t0; t < n_qt; ++t) {
+        const bool odd = (t - t0) & 1;
+        const unsigned char* qb = odd ? qb1 : qb0;
+        const unsigned char* ob = odd ? ob1 : ob0;
+        const float* lb = odd ? lb1 : lb0;
+        const float* dlb = odd ? db1 : db0;
+        const bool more = t + 1 < n_qt;
+        if (more) fetch(t + 1);
+        const bool masked = CAUSAL && t < t_mask_end;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {   // 32 queries at a time
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < C::kDSteps; ++ds) {
+                const h8 aq = *reinterpret_cast<const h8*>(qb + sw.b[ds & 1] + sw_imm(ds, blk));
+                s = mfma(aq, kf[ds], s);
+                const h8 ao = *reinterpret_cast<const h8*>(ob + sw.b[ds & 1] + sw_imm(ds, blk));
+                dp = mfma(ao, vf[ds], dp);
+            }
+            // Register r = 4g + k of this lane: query t*64 + 32*blk + 8g + 4*hi + k.
+            h8 pf[2], dsf[2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 L = *reinterpret_cast<const float4*>(lb + 32 * blk + 8 * g + 4 * hi);
+                const float4 Dl = *reinterpret_cast<const float4*>(dlb + 32 * blk + 8 * g + 4 * hi);
+                const float lv[4] = {L.x, L.y, L.z, L.w};
+                const float dv4[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = 4 * g + k;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lv[k]));
+                    if (masked && my_k > t * kBK + 32 * blk + 8 * g + 4 * hi + k) p = 0.f;
+                    pf[r >> 3][r & 7] = (_Float16)p;
+                    dsf[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dv4[k]));
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int db = 0; db < C::kDBlocks; ++db) {
+                    const int imm = tr_imm(2 * blk + kk, db);
+                    dv[db] = mfma(read_tr_operand(ob, tr, imm), pf[kk], dv[db]);
+                    dk[db] = mfma(read_tr_operand(qb, tr, imm), dsf[kk], dk[db]);
+                }
+            }
+        }
+        if (more) {
+            if (odd) put(qb0, ob0, lb0, db0);
+            else put(qb1, ob1, lb1, db1);
+        }
+        __syncthreads();
+    }
+    store_rows<D>(make_rsrc(dK + head, head_bytes), my_k, hi, dk, sigma);
+    store_rows<D>(make_rsrc(dV + head, head_bytes), my_k, hi, dv, 1.0f);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N,
+                  float c2, float sigma, hipStream_t stream) {
+    using C = BwdCfg<D>;
+    const int n_tiles = (N + C::kRows - 1) / C::kRows;
+    const int n_wg = n_tiles * BH;
+    const auto* Q = static_cast<const _Float16*>(q);
+    const auto* K = static_cast<const _Float16*>(k);
+    const auto* V = static_cast<const _Float16*>(v);
+    const auto* dO = static_cast<const _Float16*>(dout);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream, Q,
+                       K, V, static_cast<const _Float16*>(o), dO, lse, static_cast<_Float16*>(dq),
+                       delta, N, n_tiles, n_wg, c2, sigma);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
+                       Q, K, V, dO, lse, static_cast<const float*>(delta),
+                       static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
+                       c2, sigma);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      float* delta, int BH, int N, int d, float scale, bool causal,
+                      hipStream_t stream) {
+    // As in the forward, a |scale| below the smallest normal float is run as
+    // scale 0 (uniform weights over the visible keys, zero dQ and dK).
+    const double a = std::fabs(static_cast<double>(scale));
+    const float sigma = a >= 1.17549435082228751e-38 ? scale : 0.0f;
+    const float c2 = static_cast<float>(static_cast<double>(sigma) * 1.4426950408889634);
+#define FA2_BWD_CASE(DD)                                                                        \
+    case DD:                                                                                    \
+        return causal ? launch<DD, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, c2,   \
+                                         sigma, stream)                                         \
+                      : launch<DD, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, c2,  \
+                                          sigma, stream);
+    switch (d) {
+        FA2_BWD_CASE(32)
+        FA2_BWD_CASE(64)
+        FA2_BWD_CASE(96)
+        FA2_BWD_CASE(128)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef FA2_BWD_CASE
+}
+
+}  // namespace fa2

@@ -66,15 +66,9 @@
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2;
 //    causal grids start with the longest rows.
 
-// LDS tile layouts, both in 16-byte chunks (8 fp16 of one row):
-//  K: chunk-major, chunk c of key row r at (c * 64 + r) * 16.  A
-//     ds_read_b128 quarter-wave reads one chunk of 16 consecutive keys,
-//     256 contiguous bytes: every bank once.
-//  V: chunk-major with an XOR swizzle of the row, chunk c of row r at
-//     (c * 64 + (r ^ 4 * (c & 3))) * 16.  A ds_read_b64_tr_b16 half-wave
-//     reads 4 rows x 4 chunks; the XOR moves the 4 chunk planes (1 KiB
-//     apart, so on the same banks) onto 4 different 64-byte bank windows.
-// Both keep every per-lane address a lane base plus a compile-time offset.
+// LDS tile layouts (fa2_device.h): K chunk-major, V swizzled (chunk-major
+// with an XOR of the row) for the transposing reads.  Both keep every
+// per-lane address a lane base plus a compile-time offset.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -82,25 +76,17 @@
 #include <cmath>
 #include <type_traits>
 
+#include "fa2_device.h"
 #include "fa2_launch.h"
 
 namespace fa2 {
 namespace {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef __fp16 tr4 __attribute__((vector_size(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
-constexpr int kQW = 32;             // query rows per wave
-constexpr int kBK = 64;             // keys per K/V tile
-constexpr float kLn2 = 0.69314718055994530942f;
 // A tile keeps the row's reference max while the row's weights in it sum to
 // at most 2^kLazy, so every weight stays <= 2^8, far inside fp16 range.
 constexpr float kLazyBound = 256.0f;   // 2^kLazy, kLazy = 8
-constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kAhead = 4;                // LDS operand reads in flight ahead of the MFMAs
 
 template <int D>
@@ -141,37 +127,6 @@ struct Cfg {
     }
 };
 
-__device__ __forceinline__ int lds_k_off(int ch, int row) { return (ch * 64 + row) << 4; }
-__device__ __forceinline__ int lds_v_off(int ch, int row) {
-    return (ch * 64 + (row ^ ((ch & 3) << 2))) << 4;
-}
-
-// max / sum of x over the lane pair (l, l^32) that shares a query row.
-__device__ __forceinline__ float pair_max(float x) {
-    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __builtin_fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-__device__ __forceinline__ h4 lds_read_tr(const unsigned char* p) {
-    tr4 r = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-        (__attribute__((address_space(3))) tr4*)(p));
-    return __builtin_bit_cast(h4, r);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
-}
-
-// Keeps a value computed at this point of the instruction stream: the empty
-// volatile asm reads and redefines it, so the computation can be neither sunk
-// nor hoisted past the neighbouring scheduling barriers.
-template <typename T>
-__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(Cfg<D>::kThreads)
 __attribute__((amdgpu_waves_per_eu(Cfg<D>::kWavesPerSimd, Cfg<D>::kWavesPerSimd)))
@@ -194,7 +149,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 
     // Logical tile id: consecutive ids (the Q tiles of one head) go to one XCD.
     const int wg = blockIdx.x;
-    const int logical = (n_wg & 7) == 0 ? (wg & 7) * (n_wg >> 3) + (wg >> 3) : wg;
+    const int logical = xcd_logical_id(wg, n_wg);
     const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
     int qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
     if (CAUSAL) qt = n_qtiles - 1 - qt;   // longest rows first
@@ -252,14 +207,8 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Per-lane LDS read bases; the unrolled loops add compile-time offsets.
     // K (A operand of S^T): key 32*kb + l32, chunk 2*ds + hi.
     const int k_base = lds_k_off(hi, l32);
-    // V^T (A operand of O^T) via ds_read_b64_tr_b16: lane = 16*g + 4*e + cc
-    // reads keys 16*ks + 8*ab + 4*hi + e, columns 32*db + 16*(g&1) + 4*cc.
-    // Chunk 4*db + tr_ch has (chunk & 3) == tr_ch, so the swizzle stays in
-    // the base.
-    const int tr_g = lane >> 4, tr_e = (lane >> 2) & 3, tr_c = lane & 3;
-    const int tr_ch = 2 * (tr_g & 1) + (tr_c >> 1);
-    const int v_base0 = lds_v_off(tr_ch, 4 * hi + tr_e) + (tr_c & 1) * 8;
-    const int v_base1 = lds_v_off(tr_ch, 8 + 4 * hi + tr_e) + (tr_c & 1) * 8;
+    // V^T (A operand of O^T) via ds_read_b64_tr_b16 (TrBase).
+    const TrBase vt(lane);
 
     // Keys at or beyond N, and under the causal mask keys after the query,
     // get -inf.  Accumulator element (kb, r) is key k0 + 32kb + 8(r/4) +
@@ -345,10 +294,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         auto read = [&](int p) {
             if (p < C::kPV) {
                 const int ks = p / C::kDBlocks, db = p % C::kDBlocks;
-                const int imm = ((4 * db) * 64 + 16 * ks) << 4;
-                const h4 ta = lds_read_tr(vb_read + v_base0 + imm);
-                const h4 tb = lds_read_tr(vb_read + v_base1 + imm);
-                ring[p % (kAhead + 1)] = __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7);
+                ring[p % (kAhead + 1)] = read_tr_operand(vb_read, vt, tr_imm(ks, db));
             } else {
                 const int j = p - C::kPV, ds = j >> 1, kb = j & 1;
                 ring[p % (kAhead + 1)] = *reinterpret_cast<const h8*>(kb_read + k_base + lds_k_off(2 * ds, 32 * kb));
@@ -479,11 +425,8 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
             for (int db = 0; db < C::kDBlocks; ++db) {
-                const int imm = ((4 * db) * 64 + 16 * ks) << 4;
-                const h4 ta = lds_read_tr(vb_read + v_base0 + imm);
-                const h4 tb = lds_read_tr(vb_read + v_base1 + imm);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    __builtin_shufflevector(ta, tb, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], oacc[db], 0, 0, 0);
+                    read_tr_operand(vb_read, vt, tr_imm(ks, db)), pf[ks], oacc[db], 0, 0, 0);
             }
         }
     }

@@ -11,4 +11,11 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o,
                       float* lse, int BH, int N, int d, float scale,
                       bool causal, hipStream_t stream);
 
+// Launch the two backward kernels (dQ + delta, then dK/dV) for
+// already-validated arguments, in order on `stream`.
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      float* delta, int BH, int N, int d, float scale, bool causal,
+                      hipStream_t stream);
+
 }  // namespace fa2

@@ -1,5 +1,6 @@
 /*
- * fa2.h -- C ABI of the FlashAttention-2 forward pass for AMD MI355X (gfx950).
+ * fa2.h -- C ABI of the FlashAttention-2 forward pass, and its backward pass,
+ * for AMD MI355X (gfx950).
  *
  * The operation is exact scaled-dot-product attention of one head, for every
  * (batch, head) pair:
@@ -18,7 +19,8 @@
  * normalises once at the end.
  *
  * All functions are plain C, thread-safe and re-entrant; the library keeps no
- * state between calls and allocates no device memory.
+ * state between calls and allocates no device memory (the backward pass
+ * takes its one workspace, delta, from the caller).
  */
 #ifndef FA2_H_
 #define FA2_H_
@@ -27,12 +29,13 @@
 extern "C" {
 #endif
 
-/* Status codes returned by fa2_fwd. */
+/* Status codes returned by fa2_fwd and fa2_bwd. */
 typedef enum {
     FA2_OK = 0,
     FA2_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, grid too large,
                                 non-finite scale, output aliasing an input     */
-    FA2_ERR_UNSUPPORTED = 2, /* head dim not one of 32, 64, 96, 128, 256       */
+    FA2_ERR_UNSUPPORTED = 2, /* head dim not one of 32, 64, 96, 128, 256
+                                (fa2_bwd: 32, 64, 96, 128)                     */
     FA2_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned                  */
     FA2_ERR_NO_DEVICE = 4,   /* no usable gfx950 device / HIP runtime failure  */
     FA2_ERR_LAUNCH = 5       /* the kernel launch failed                       */
@@ -68,6 +71,43 @@ typedef enum {
  * NaN or Inf inputs are outside the contract and propagate per IEEE rules.
  */
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa2_bwd -- gradients of the forward pass, asynchronous on `stream`.
+ *
+ * For an upstream gradient dO of O, returns the gradients of <dO, O> (the
+ * sum of dO * O over all elements) with respect to Q, K and V:
+ *
+ *     P  = exp(scale * Q K^T - LSE)  (masked entries 0)
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta_i = dO_i . O_i
+ *     dQ = scale * dS K,  dK = scale * dS^T Q
+ *
+ * S and P are recomputed tile by tile from Q, K and the forward's LSE,
+ * never stored ("3.6 Attention I -- the memory problem and FlashAttention
+ * principles", 3.6.7: the backward recomputes S and P from the O(N) row
+ * statistics kept by the forward; the formulas are the chain rule through
+ * the row softmax).
+ *
+ *   q, k, v : device pointers, fp16 [B, H, N, d], the forward's inputs.
+ *   o, lse  : device pointers, the forward's outputs for the same q, k, v,
+ *             scale and causal (fp16 [B, H, N, d] and fp32 [B, H, N]).
+ *   dout    : device pointer, fp16 [B, H, N, d], the upstream gradient dO.
+ *   dq, dk, dv : device pointers, fp16 [B, H, N, d].  Written: every
+ *             element, rounded once to fp16 (round to nearest even).
+ *   delta   : device pointer, fp32 [B, H, N], caller-owned workspace.
+ *             Written: delta_i = sum_c dO_ic * O_ic of each query row, which
+ *             the second of the two kernels reads.
+ *   B, H, N, scale, causal, stream : as for fa2_fwd.
+ *   d       : head dimension: 32, 64, 96 or 128.
+ *
+ * Ownership: the caller allocates and owns all buffers.  dq, dk, dv and delta
+ * must not overlap any input (q, k, v, o, lse, dout) nor each other.
+ * Alignment: all pointers 16-byte aligned.  Errors as for fa2_fwd; all
+ * argument checks run before the first HIP call.
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta,
             int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

@@ -39,7 +39,11 @@ import numpy as np
 
 from .attention import _masked_scores, _sigma, _stable_softmax_parts, oracle_threads
 
-__all__ = ["attention_bwd_fp64"]
+__all__ = ["attention_bwd_fp64", "attention_bwd_error_scale"]
+
+# Absolute rounding error of an fp16 subnormal (2^-25) in units of the
+# relative one (u = 2^-11).
+_SUBNORMAL = 2.0 ** -14
 
 
 def _bwd_rows(q_rows, row_ids, k, v, do_rows, sigma, causal):
@@ -117,3 +121,81 @@ def attention_bwd_fp64(q, k, v, do, scale, causal=False, threads=None, row_block
         for bh in range(B * H):
             one_head(bh)
     return dq, dk, dv, delta
+
+
+def attention_bwd_error_scale(q, k, v, do, scale, causal=False, threads=None, row_block=None):
+    """Per-element error scales E of dQ, dK, dV and delta, float64.
+
+    Not part of what the kernels compute: the scale that a tolerance on
+    their result is measured in.  A sum of products whose factors carry a
+    relative error u (here u = 2^-11, fp16 rounding) is off by at most
+    about u * sum |a| |b| -- the standard forward-error bound of a dot
+    product.  Rounding to fp16 with gradual underflow gives
+    fl(x) = x (1 + e) + a with |e| <= u and |a| <= 2^-25 (half the subnormal
+    spacing), so a rounded factor x contributes u |x| + 2^-25, i.e.
+    u (|x| + 2^-14 M) with M the visibility mask.  The gradients' factors
+    that are rounded to fp16 on the way (P, dS), and the error of delta
+    (taken from the fp16 O), give
+
+        E_dV    = (|P| + t M)^T |dO|
+        E_dQ    = |sigma| ((|dS| + t M) |K| + Dabs_i (|P| |K|))
+        E_dK    = |sigma| ((|dS| + t M)^T |Q| + (|P| Dabs)^T |Q|)
+        E_delta = Dabs_i = sum_c |dO_ic| |O_ic|,          t = 2^-14,
+
+    where the Dabs terms bound how an error u * Dabs_i in delta_i moves
+    dS_ij = P_ij (dP_ij - delta_i).  Where the gradient is a small
+    difference of large terms (Q and K sharing a large component, or a
+    constant V) E is much larger than |G|; elsewhere it is close to it.
+    Same arguments as ``attention_bwd_fp64``; returns (E_dq, E_dk, E_dv,
+    E_delta).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    B, H, N, d = q.shape
+    sigma = abs(_sigma(scale))
+    if row_block is None:
+        row_block = max(1, (1 << 21) // max(N, 1))
+    e_dq = np.empty((B, H, N, d), dtype=np.float64)
+    e_dk = np.empty((B, H, N, d), dtype=np.float64)
+    e_dv = np.empty((B, H, N, d), dtype=np.float64)
+    e_dl = np.empty((B, H, N), dtype=np.float64)
+
+    def one_head(bh):
+        b, h = divmod(bh, H)
+        qh = q[b, h].astype(np.float64)
+        kh = k[b, h].astype(np.float64)
+        vh = v[b, h].astype(np.float64)
+        doh = do[b, h].astype(np.float64)
+        ak = np.abs(kh)
+        acc_k = np.zeros((N, d))
+        acc_v = np.zeros((N, d))
+        for r0 in range(0, N, row_block):
+            ids = np.arange(r0, min(r0 + row_block, N))
+            s = _masked_scores(qh[ids], ids, kh, _sigma(scale), causal)
+            _, e, l = _stable_softmax_parts(s)
+            p = e / l[:, None]
+            vis = np.isfinite(s) * _SUBNORMAL
+            dp = doh[ids] @ vh.T
+            dl = (p * dp).sum(axis=1)
+            ads = np.abs(p * (dp - dl[:, None])) + vis
+            dabs = (np.abs(doh[ids]) * np.abs(p @ vh)).sum(axis=1)
+            aq = np.abs(qh[ids])
+            e_dq[b, h, ids] = sigma * (ads @ ak + dabs[:, None] * (p @ ak))
+            acc_k += sigma * (ads.T @ aq + (p * dabs[:, None]).T @ aq)
+            acc_v += (p + vis).T @ np.abs(doh[ids])
+            e_dl[b, h, ids] = dabs
+        e_dk[b, h] = acc_k
+        e_dv[b, h] = acc_v
+
+    nthreads = threads or oracle_threads()
+    if nthreads > 1 and B * H > 1:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            with ThreadPoolExecutor(max_workers=nthreads) as ex:
+                list(ex.map(one_head, range(B * H)))
+    else:
+        for bh in range(B * H):
+            one_head(bh)
+    return e_dq, e_dk, e_dv, e_dl
