@@ -2,6 +2,7 @@
 """Throughput of the FlashAttention-2 forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ref] [--pass fwd|bwd]
+                    [--impl fa2|fa1] [--batch-sweep]
 
 Without --warmup / --steps, W fills about 0.4 s and K about 0.25 s of
 launches (the GPU's clock needs ~0.1 s of load to settle; a short kernel
@@ -28,6 +29,12 @@ dQ kernel, then the dK/dV kernel) on the forward's O and LSE and a seeded
 upstream gradient; FLOPs = 10*B*H*N^2*d (five products of 2*N^2*d: S, dP,
 dV, dK, dQ; halved when causal), the roofline unit is the whole call, and
 the CPU baseline is the float64 gradient oracle.
+
+--impl fa1 times the FlashAttention-1-order comparator (fa1_fwd, d = 64)
+on the workload instead of fa2_fwd.  --batch-sweep times both, causal and
+not, at [B, 32, 2048, 64] for B = 1, 2, 4, 8, 16 (the batch experiment of
+"Implementing FlashAttention 1 and 2 forward in Triton") and prints one JSON
+line with every point and the FA2 / FA1 speed ratios.
 """
 from __future__ import annotations
 
@@ -47,7 +54,8 @@ METRIC = "FA2 fwd TFLOP/s and % of MI355X fp16 MFMA peak, [4,32,2048,64]"
 METRIC_BWD = "FA2 bwd TFLOP/s and % of MI355X fp16 MFMA peak"
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_fwd_amd", "csrc", f)
-                  for f in ("fa2_fwd_gfx950.hip", "fa2_bwd_gfx950.hip", "fa2_device.h", "fa2_api.cpp",
+                  for f in ("fa2_fwd_gfx950.hip", "fa2_bwd_gfx950.hip", "fa1_fwd_gfx950.hip",
+                            "fa2_device.h", "fa2_api.cpp",
                             "fa2_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -147,6 +155,67 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
             "seconds": round(dt, 3)}
 
 
+def time_calls(step, sync, warmup=None, steps=None):
+    """Warm up (default ~0.4 s) and time (default ~0.25 s) back-to-back calls;
+    returns (steps, warmup, seconds per call)."""
+    n_probe = 5
+    sync()
+    tp0 = time.perf_counter()
+    for _ in range(n_probe):
+        step()
+    sync()
+    t_one = max((time.perf_counter() - tp0) / n_probe, 1e-6)
+    warmup = max(20, math.ceil(0.4 / t_one)) if warmup is None else warmup
+    steps = max(10, math.ceil(0.25 / t_one)) if steps is None else steps
+    for _ in range(max(0, warmup - n_probe)):
+        step()
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    sync()
+    return steps, warmup, (time.perf_counter() - t0) / steps
+
+
+def batch_sweep(torch, fa2):
+    """FA2 vs the FA1 loop order at [B, 32, 2048, 64], B = 1 .. 16."""
+    from exact_attention_fwd_amd.workloads import make_qkv
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    H, N, d = 32, 2048, 64
+    points = []
+    for B in (1, 2, 4, 8, 16):
+        tq, tk, tv = (torch.from_numpy(x).to(dev) for x in make_qkv(B, H, N, d, 1.0, 0))
+        out = torch.empty_like(tq)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ws_bytes = fa2.fa1_workspace_bytes(B, H, N, d)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        for causal in (False, True):
+            row = {"B": B, "H": H, "N": N, "d": d, "causal": causal}
+            for impl in ("fa2", "fa1"):
+                if impl == "fa2":
+                    a = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, d ** -0.5, causal, stream.cuda_stream)
+                    call = fa2.fa2_fwd
+                else:
+                    a = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         ws.data_ptr(), ws_bytes, B, H, N, d, d ** -0.5, causal, stream.cuda_stream)
+                    call = fa2.fa1_fwd
+
+                def step():
+                    if call(*a) != fa2.FA2_OK:
+                        raise RuntimeError(f"{impl} failed")
+                _, _, sec = time_calls(step, lambda: torch.cuda.synchronize(dev))
+                flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
+                row[f"{impl}_ms"] = round(sec * 1e3, 5)
+                row[f"{impl}_tflops"] = round(flops / sec / 1e12, 2)
+            row["fa2_over_fa1"] = round(row["fa1_ms"] / row["fa2_ms"], 3)
+            log(f"[sweep] {row}")
+            points.append(row)
+    return points
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +224,10 @@ def main():
     ap.add_argument("--workload", default="ref")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward pass")
+    ap.add_argument("--impl", choices=("fa2", "fa1"), default="fa2",
+                    help="forward implementation: fa2_fwd (default) or the FA1-order comparator")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="instead: FA2 vs FA1 order at [B,32,2048,64], B = 1..16, one JSON line")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -185,6 +258,12 @@ def main():
     import exact_attention_fwd_amd as fa2
     from exact_attention_fwd_amd.workloads import WORKLOADS, make_qkv, sample_rows
 
+    if args.batch_sweep:
+        points = batch_sweep(torch, fa2)
+        print(json.dumps({"metric": "FA2 vs FA1-order forward time, [B,32,2048,64] fp16",
+                          "unit": "ms", "points": points}), flush=True)
+        return
+
     w = WORKLOADS[args.workload]
     log(f"[bench] workload {w.name} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
     q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.sigma, w.seed)
@@ -197,7 +276,14 @@ def main():
     # One validated call through the torch wrapper, then the timed steps call
     # the C entry point itself with the same (cached) pointers and stream.
     fa2.fwd(tq, tk, tv, scale=w.scale, causal=w.causal, out=out, lse=lse)
-    if args.which == "fwd":
+    if args.which == "fwd" and args.impl == "fa1":
+        ws_bytes = fa2.fa1_workspace_bytes(w.B, w.H, w.N, w.d)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        entry = fa2.fa1_fwd
+        args_c = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  ws.data_ptr(), ws_bytes, w.B, w.H, w.N, w.d, w.scale, w.causal,
+                  stream.cuda_stream)
+    elif args.which == "fwd":
         entry = fa2.fa2_fwd
         args_c = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
                   w.B, w.H, w.N, w.d, w.scale, w.causal, stream.cuda_stream)
@@ -253,7 +339,8 @@ def main():
         f"{value:.1f} TFLOP/s ({100 * value / PEAK_FP16_TFLOPS:.1f}% of peak)")
 
     result = {
-        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
+        "metric": (METRIC_BWD if args.which == "bwd" else
+                   METRIC if args.impl == "fa2" else "FA1-order fwd TFLOP/s (comparator)"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -272,12 +359,15 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name if args.which == "fwd" else f"bwd:{w.name}"),
+                     "traffic": measured_traffic(w.name if args.which == "fwd" and args.impl == "fa2"
+                                                 else f"{args.which}-{args.impl}:{w.name}"),
                      "launch_ms": round(ev_ms, 5)},
     }
 
     if args.which == "bwd":
         result["config"]["pass"] = "backward (dQ, dK, dV, delta)"
+    if args.impl == "fa1":
+        result["config"]["impl"] = "FA1 loop order (fa1_fwd)"
     if not args.no_parity and args.which == "bwd":
         # the first two heads of the timed output, every element, in units of
         # each gradient's rounding-error bound u (|G| + E + 2^-14)

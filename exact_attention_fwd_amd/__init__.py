@@ -3,7 +3,9 @@
 ``fwd(q, k, v, scale=None, causal=False) -> (o, lse)`` runs the library's
 hand-written gfx950 kernels on torch fp16 tensors, ``bwd(q, k, v, o, lse,
 dout, ...) -> (dq, dk, dv, delta)`` their gradients; ``fa2_fwd`` and
-``fa2_bwd`` are the C entry points themselves (raw device addresses).  The seeded synthetic workloads live in
+``fa2_bwd`` are the C entry points themselves (raw device addresses).
+``fwd_fa1`` / ``fa1_fwd`` compute the same forward in the FlashAttention-1
+loop order, the comparator of the FA2 kernel.  The seeded synthetic workloads live in
 ``exact_attention_fwd_amd.workloads``.
 """
 from ._lib import (  # noqa: F401
@@ -17,11 +19,14 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     Fa2Error,
     bwd,
+    fa1_fwd,
+    fa1_workspace_bytes,
     fa2_bwd,
     fa2_fwd,
     fa2_last_hip_error,
     fa2_status_string,
     fa2_version,
     fwd,
+    fwd_fa1,
     load_library,
 )

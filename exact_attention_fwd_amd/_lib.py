@@ -19,7 +19,8 @@ FA2_ERR_MISALIGNED = 3
 FA2_ERR_NO_DEVICE = 4
 FA2_ERR_LAUNCH = 5
 
-EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_status_string", "fa2_last_hip_error", "fa2_version")
+EXPORTED = ("fa2_fwd", "fa2_bwd", "fa1_fwd", "fa1_workspace_bytes", "fa2_status_string",
+            "fa2_last_hip_error", "fa2_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -50,6 +51,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.fa2_bwd.restype = ctypes.c_int
+        lib.fa1_fwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_size_t] + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa1_fwd.restype = ctypes.c_int
+        lib.fa1_workspace_bytes.argtypes = [ctypes.c_int] * 4
+        lib.fa1_workspace_bytes.restype = ctypes.c_size_t
         lib.fa2_status_string.argtypes = [ctypes.c_int]
         lib.fa2_status_string.restype = ctypes.c_char_p
         lib.fa2_last_hip_error.argtypes = []
@@ -72,6 +78,16 @@ def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal,
     """The C entry point, same arguments (device addresses as ints)."""
     return load_library().fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H),
                                   int(N), int(d), float(scale), int(bool(causal)), stream)
+
+
+def fa1_fwd(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, scale, causal, stream) -> int:
+    """The C entry point of the FlashAttention-1-order comparator."""
+    return load_library().fa1_fwd(q, k, v, o, lse, ws, int(ws_bytes), int(B), int(H), int(N),
+                                  int(d), float(scale), int(bool(causal)), stream)
+
+
+def fa1_workspace_bytes(B, H, N, d) -> int:
+    return load_library().fa1_workspace_bytes(int(B), int(H), int(N), int(d))
 
 
 def fa2_status_string(status: int) -> str:
@@ -170,3 +186,30 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
         raise Fa2Error(status, f"fa2_bwd failed: {fa2_status_string(status)} "
                                f"(hip error {fa2_last_hip_error()})")
     return dq, dk, dv, delta
+
+
+def fwd_fa1(q, k, v, scale=None, causal=False, out=None, lse=None, workspace=None, stream=None):
+    """The same forward pass in the FlashAttention-1 loop order (the
+    comparator of ``fwd``).  ``workspace`` is a uint8 CUDA tensor of at least
+    fa1_workspace_bytes(B, H, N, d) bytes (allocated if None).  Returns
+    (o, lse)."""
+    import torch
+
+    _check_qkv((("q", q), ("k", k), ("v", v)))
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    out = _out(out, q, torch.float16, q.shape, "out")
+    lse = _out(lse, q, torch.float32, (B, H, N), "lse")
+    need = fa1_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = fa1_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, N,
+                     d, scale, causal, stream)
+    if status != FA2_OK:
+        raise Fa2Error(status, f"fa1_fwd failed: {fa2_status_string(status)} "
+                               f"(hip error {fa2_last_hip_error()})")
+    return out, lse

@@ -103,6 +103,39 @@ extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* 
                                          scale, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" size_t fa1_workspace_bytes(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    return fa2::fa1_workspace_floats(B * H, N, d) * sizeof(float);
+}
+
+extern "C" int fa1_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                       size_t ws_bytes, int B, int H, int N, int d, float scale, int causal,
+                       void* stream) {
+    if (!q || !k || !v || !o || !lse || !ws) return FA2_ERR_INVALID_ARG;
+    if (const int st = check_sizes(B, H, N, d, scale, /*max_d=*/256)) return st;
+    if (d != 64) return FA2_ERR_UNSUPPORTED;
+    // fp32 per-head offsets of the workspace are 32-bit: N * d * 4 < 2^31.
+    if (int64_t(N) * d > (int64_t(1) << 27)) return FA2_ERR_INVALID_ARG;
+    const size_t rows = size_t(B) * H * N;
+    const size_t t_bytes = rows * size_t(d) * 2;
+    const size_t l_bytes = rows * 4;
+    const size_t w_bytes = fa2::fa1_workspace_floats(B * H, N, d) * sizeof(float);
+    if (ws_bytes < w_bytes) return FA2_ERR_INVALID_ARG;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(ws);
+    if (bits & 15u) return FA2_ERR_MISALIGNED;
+    const struct { const void* p; size_t n; } outs[] = {{o, t_bytes}, {lse, l_bytes}, {ws, w_bytes}};
+    for (const auto& w : outs) {
+        for (const void* in : {q, k, v})
+            if (overlaps(w.p, w.n, in, t_bytes)) return FA2_ERR_INVALID_ARG;
+        for (const auto& w2 : outs)
+            if (&w2 != &w && overlaps(w.p, w.n, w2.p, w2.n)) return FA2_ERR_INVALID_ARG;
+    }
+    return launch_status(fa2::launch_fa1(q, k, v, o, lse, ws, B * H, N, d, scale, causal != 0,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char* fa2_status_string(int status) {
     switch (status) {
         case FA2_OK: return "ok";

@@ -18,4 +18,10 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       float* delta, int BH, int N, int d, float scale, bool causal,
                       hipStream_t stream);
 
+// The FlashAttention-1 loop order (the comparator): workspace of
+// fa1_workspace_floats(BH, N, d) floats (fp32 O, then m, then l).
+size_t fa1_workspace_floats(int BH, int N, int d);
+hipError_t launch_fa1(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                      int BH, int N, int d, float scale, bool causal, hipStream_t stream);
+
 }  // namespace fa2

@@ -25,6 +25,8 @@
 #ifndef FA2_H_
 #define FA2_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -109,6 +111,34 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
             const void* dout, void* dq, void* dk, void* dv, float* delta,
             int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa1_fwd -- the same forward pass (same outputs, within the same tolerance)
+ * computed in the FlashAttention-1 loop order, as a comparator for fa2_fwd.
+ *
+ * "Implementing FlashAttention 1 and 2 forward in Triton", sections
+ * "parallelisation unit" and "output accumulation": one program per
+ * (batch, head); key/value blocks in the outer loop, every query block in the
+ * inner one; after each key/value block the normalised output and the row
+ * statistics (m, l) are written to global memory in fp32 and read back for
+ * the next block; fp16 only at the end.  Here: one workgroup per
+ * (batch, head), 128-key blocks, the fp32 state in `ws`.
+ *
+ *   q, k, v, o, lse, B, H, N, scale, causal, stream : as for fa2_fwd.
+ *   d       : 64 only.  N * d <= 2^27.
+ *   ws      : device pointer, caller-owned workspace of at least
+ *             fa1_workspace_bytes(B, H, N, d) bytes (fp32 O, m and l of
+ *             every row); its contents on entry are ignored, on return
+ *             undefined.  ws_bytes is its size.
+ * Errors as for fa2_fwd; a workspace that is too small, or overlaps q, k,
+ * v, o or lse, is FA2_ERR_INVALID_ARG.
+ */
+int fa1_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+            size_t ws_bytes, int B, int H, int N, int d, float scale, int causal,
+            void* stream);
+
+/* Workspace bytes fa1_fwd needs: B * H * N * (d + 2) * 4 (0 for bad sizes). */
+size_t fa1_workspace_bytes(int B, int H, int N, int d);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa2_status_string(int status);

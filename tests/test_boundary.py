@@ -25,7 +25,7 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa[12]_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -168,3 +168,30 @@ def test_bwd_inputs_may_alias_each_other(lib):
     # q = k = v is a valid call; with a misaligned delta (checked after the
     # overlap rules are reachable only for valid pointers) it stops before HIP.
     assert bcall(k=Q, v=Q, delta=DELTA + 4) == fa2.FA2_ERR_MISALIGNED
+
+
+# ------------------------------------------------------------------ fa1_fwd
+WS = 12 << 20
+
+
+def fcall(q=Q, k=K, v=V, o=O, lse=L, ws=WS, ws_bytes=None, **kw):
+    a = dict(GOOD, **kw)
+    if ws_bytes is None:
+        ws_bytes = fa2.fa1_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+    return fa2.fa1_fwd(q, k, v, o, lse, ws, ws_bytes, a["B"], a["H"], a["N"], a["d"], a["scale"],
+                       a["causal"], 0)
+
+
+def test_fa1_workspace_size():
+    assert fa2.fa1_workspace_bytes(2, 3, 100, 64) == 2 * 3 * 100 * 66 * 4
+    assert fa2.fa1_workspace_bytes(0, 3, 100, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=128), "FA2_ERR_UNSUPPORTED"), (dict(d=32), "FA2_ERR_UNSUPPORTED"),
+    (dict(ws=0), "FA2_ERR_INVALID_ARG"), (dict(ws_bytes=100), "FA2_ERR_INVALID_ARG"),
+    (dict(N=(1 << 21) + 64), "FA2_ERR_INVALID_ARG"), (dict(ws=WS + 4), "FA2_ERR_MISALIGNED"),
+    (dict(ws=Q + 16), "FA2_ERR_INVALID_ARG"), (dict(ws=O + 16), "FA2_ERR_INVALID_ARG"),
+    (dict(scale=math.nan), "FA2_ERR_INVALID_ARG")])
+def test_fa1_rejects(lib, kw, status):
+    assert fcall(**kw) == getattr(fa2, status)
