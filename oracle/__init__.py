@@ -8,8 +8,9 @@ two meet only in the seeded input generators, which hold none of the method's
 arithmetic.
 
 Everything here is plain float64 numpy (plus one pure-Python brute force for
-tiny cases).  See ``oracle.attention`` (forward) and ``oracle.attention_bwd``
-(gradients) for the functions and the passages of the pages each one follows.
+tiny cases).  See ``oracle.attention`` (forward), ``oracle.attention_bwd``
+(gradients) and ``oracle.merge`` (merging partial results over key parts) for
+the functions and the passages of the pages each one follows.
 """
 from .attention import (
     attention_fp64,
@@ -18,6 +19,7 @@ from .attention import (
     brute_force_attention,
 )
 from .attention_bwd import attention_bwd_fp64
+from .merge import merge_lse_fp64
 
 __all__ = [
     "attention_fp64",
@@ -25,4 +27,5 @@ __all__ = [
     "online_softmax_attention",
     "brute_force_attention",
     "attention_bwd_fp64",
+    "merge_lse_fp64",
 ]

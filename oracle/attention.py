@@ -113,7 +113,10 @@ def attention_fp64(q, k, v, scale, causal=False, rows=None, return_stats=False,
     """Materialised softmax attention in float64, the definition itself.
 
     Arguments
-      q, k, v : arrays [B, H, N, d] (fp16 inputs are widened exactly).
+      q, k, v : arrays [B, H, N, d] (fp16 inputs are widened exactly).  Without
+                the causal mask the keys may be a different number Nk: q is
+                [B, H, N, d], k and v [B, H, Nk, d] (a short query block
+                against a long key/value cache; every query sees every key).
       scale   : the softmax scale (1/sqrt(d) in the workloads); used as the
                 fp32 value the kernel receives.
       causal  : mask key j for query i when j > i.
@@ -129,8 +132,11 @@ def attention_fp64(q, k, v, scale, causal=False, rows=None, return_stats=False,
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
-    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if causal and q.shape[2] != k.shape[2]:
+        raise ValueError("causal attention needs as many queries as keys")
     B, H, N, d = q.shape
     sigma = _sigma(scale)
     if rows is None:
@@ -289,7 +295,8 @@ def brute_force_attention(q, k, v, scale, causal=False):
     written with exactly rounded sums and no numpy arithmetic, so that a slip
     in the vectorised oracle (a transposed operand, a wrong mask index, a
     missing term) shows up as a mismatch.  Inputs are nested lists or arrays
-    [B, H, N, d]; returns (O, LSE) as nested lists of floats.
+    [B, H, N, d] (k, v may have another length when not causal); returns
+    (O, LSE) as nested lists of floats.
     """
     sigma = _sigma(scale)
     q = np.asarray(q).astype(np.float64).tolist()
@@ -300,10 +307,10 @@ def brute_force_attention(q, k, v, scale, causal=False):
         o_b, lse_b = [], []
         for h in range(len(q[b])):
             qs, ks, vs = q[b][h], k[b][h], v[b][h]
-            n, d = len(qs), len(qs[0])
+            n, nk, d = len(qs), len(ks), len(qs[0])
             o_h, lse_h = [], []
             for i in range(n):
-                visible = [j for j in range(n) if not (causal and j > i)]
+                visible = [j for j in range(nk) if not (causal and j > i)]
                 s = {j: sigma * math.fsum(qs[i][t] * ks[j][t] for t in range(d))
                      for j in visible}
                 m = max(s.values())
