@@ -19,8 +19,9 @@ FA2_ERR_MISALIGNED = 3
 FA2_ERR_NO_DEVICE = 4
 FA2_ERR_LAUNCH = 5
 
-EXPORTED = ("fa2_fwd", "fa2_bwd", "fa1_fwd", "fa1_workspace_bytes", "fa2_status_string",
-            "fa2_last_hip_error", "fa2_version")
+EXPORTED = ("fa2_fwd", "fa2_bwd", "fa1_fwd", "fa1_workspace_bytes", "fa2_fwd_splitkv",
+            "fa2_splitkv_splits", "fa2_splitkv_workspace_bytes", "fa2_lse_merge",
+            "fa2_status_string", "fa2_last_hip_error", "fa2_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -56,6 +57,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa1_fwd.restype = ctypes.c_int
         lib.fa1_workspace_bytes.argtypes = [ctypes.c_int] * 4
         lib.fa1_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa2_fwd_splitkv.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_size_t] + [
+            ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa2_fwd_splitkv.restype = ctypes.c_int
+        lib.fa2_splitkv_splits.argtypes = [ctypes.c_int] * 6
+        lib.fa2_splitkv_splits.restype = ctypes.c_int
+        lib.fa2_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 6
+        lib.fa2_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa2_lse_merge.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+        lib.fa2_lse_merge.restype = ctypes.c_int
         lib.fa2_status_string.argtypes = [ctypes.c_int]
         lib.fa2_status_string.restype = ctypes.c_char_p
         lib.fa2_last_hip_error.argtypes = []
@@ -88,6 +98,27 @@ def fa1_fwd(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, scale, causal, stream) ->
 
 def fa1_workspace_bytes(B, H, N, d) -> int:
     return load_library().fa1_workspace_bytes(int(B), int(H), int(N), int(d))
+
+
+def fa2_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d, scale, n_splits, stream) -> int:
+    """The C entry point of the split key/value forward (device addresses as ints)."""
+    return load_library().fa2_fwd_splitkv(q, k, v, o, lse, ws, int(ws_bytes), int(B), int(H),
+                                          int(Nq), int(Nk), int(d), float(scale), int(n_splits),
+                                          stream)
+
+
+def fa2_splitkv_splits(B, H, Nq, Nk, d, n_splits=0) -> int:
+    return load_library().fa2_splitkv_splits(int(B), int(H), int(Nq), int(Nk), int(d), int(n_splits))
+
+
+def fa2_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits=0) -> int:
+    return load_library().fa2_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d),
+                                                      int(n_splits))
+
+
+def fa2_lse_merge(o_parts, lse_parts, o, lse, n_parts, rows, d, stream) -> int:
+    return load_library().fa2_lse_merge(o_parts, lse_parts, o, lse, int(n_parts), int(rows),
+                                        int(d), stream)
 
 
 def fa2_status_string(status: int) -> str:
@@ -211,5 +242,63 @@ def fwd_fa1(q, k, v, scale=None, causal=False, out=None, lse=None, workspace=Non
                      d, scale, causal, stream)
     if status != FA2_OK:
         raise Fa2Error(status, f"fa1_fwd failed: {fa2_status_string(status)} "
+                               f"(hip error {fa2_last_hip_error()})")
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, scale=None, n_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Non-causal attention of q [B, H, Nq, d] over k, v [B, H, Nk, d] with
+    the keys split across workgroups (0 = the library's choice); returns
+    (o, lse).  ``workspace`` (uint8 CUDA tensor) is allocated when needed."""
+    import torch
+
+    _check_qkv((("k", k), ("v", v)))
+    _check_qkv((("q", q),))
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != d or k.device != q.device:
+        raise ValueError("k, v must be [B, H, Nk, d] on q's device")
+    if scale is None:
+        scale = d ** -0.5
+    out = _out(out, q, torch.float16, q.shape, "out")
+    lse = _out(lse, q, torch.float32, (B, H, Nq), "lse")
+    need = fa2_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), ws_ptr, ws_bytes, B, H, Nq, Nk, d, scale, n_splits,
+                             stream)
+    if status != FA2_OK:
+        raise Fa2Error(status, f"fa2_fwd_splitkv failed: {fa2_status_string(status)} "
+                               f"(hip error {fa2_last_hip_error()})")
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """Merge partial results: o_parts fp32 [S, ..., d], lse_parts fp32 [S, ...]
+    (CUDA tensors) -> (o fp16 [..., d], lse fp32 [...])."""
+    import torch
+
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts and lse_parts must be float32")
+    if not (o_parts.is_cuda and lse_parts.is_cuda and o_parts.is_contiguous()
+            and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous CUDA tensors")
+    if tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape) or o_parts.dim() < 2:
+        raise ValueError("o_parts must be [S, ..., d] and lse_parts [S, ...]")
+    S, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts.numel() // S
+    out = _out(out, o_parts, torch.float16, o_parts.shape[1:], "out")
+    lse = _out(lse, o_parts, torch.float32, lse_parts.shape[1:], "lse")
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+    status = fa2_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), S, rows, d, stream)
+    if status != FA2_OK:
+        raise Fa2Error(status, f"fa2_lse_merge failed: {fa2_status_string(status)} "
                                f"(hip error {fa2_last_hip_error()})")
     return out, lse

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <utility>
 
 #include "fa2_launch.h"
 
@@ -134,6 +135,93 @@ extern "C" int fa1_fwd(const void* q, const void* k, const void* v, void* o, flo
     }
     return launch_status(fa2::launch_fa1(q, k, v, o, lse, ws, B * H, N, d, scale, causal != 0,
                                          static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// Sizes of the split key/value call; 0 when valid.
+int check_splitkv_sizes(int B, int H, int Nq, int Nk, int d, float scale, int n_splits) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA2_ERR_INVALID_ARG;
+    if (Nq > (1 << 22) || Nk > (1 << 22)) return FA2_ERR_INVALID_ARG;
+    if (int64_t(B) * H * Nq > INT32_MAX || int64_t(B) * H * Nk > INT32_MAX) return FA2_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA2_ERR_INVALID_ARG;
+    if (n_splits < 0 || n_splits > 4096) return FA2_ERR_INVALID_ARG;
+    if (d != 32 && d != 64 && d != 96 && d != 128) return FA2_ERR_UNSUPPORTED;
+    if (int64_t(Nq) * d > (int64_t(1) << 29) || int64_t(Nk) * d > (int64_t(1) << 29))
+        return FA2_ERR_INVALID_ARG;
+    return 0;
+}
+
+size_t splitkv_ws_bytes(int B, int H, int Nq, int d, const fa2::SplitPlan& p) {
+    if (p.n_splits <= 1) return 0;
+    return size_t(p.n_splits) * size_t(B) * H * Nq * (size_t(d) + 1) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" int fa2_splitkv_splits(int B, int H, int Nq, int Nk, int d, int n_splits) {
+    if (check_splitkv_sizes(B, H, Nq, Nk, d, 1.0f, n_splits)) return 0;
+    return fa2::plan_splits(B * H, Nq, Nk, n_splits).n_splits;
+}
+
+extern "C" size_t fa2_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int n_splits) {
+    if (check_splitkv_sizes(B, H, Nq, Nk, d, 1.0f, n_splits)) return 0;
+    return splitkv_ws_bytes(B, H, Nq, d, fa2::plan_splits(B * H, Nq, Nk, n_splits));
+}
+
+extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               void* ws, size_t ws_bytes, int B, int H, int Nq, int Nk, int d,
+                               float scale, int n_splits, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+    if (const int st = check_splitkv_sizes(B, H, Nq, Nk, d, scale, n_splits)) return st;
+    const fa2::SplitPlan plan = fa2::plan_splits(B * H, Nq, Nk, n_splits);
+    // one workgroup per (32-query tile, key range, batch * head)
+    if (int64_t(B) * H * ((Nq + 31) / 32) * plan.n_splits > INT32_MAX) return FA2_ERR_INVALID_ARG;
+    const size_t w_bytes = splitkv_ws_bytes(B, H, Nq, d, plan);
+    if (w_bytes && (!ws || ws_bytes < w_bytes)) return FA2_ERR_INVALID_ARG;
+    uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                     reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                     reinterpret_cast<uintptr_t>(lse);
+    if (w_bytes) bits |= reinterpret_cast<uintptr_t>(ws);
+    if (bits & 15u) return FA2_ERR_MISALIGNED;
+    const size_t q_bytes = size_t(B) * H * Nq * size_t(d) * 2;
+    const size_t kv_bytes = size_t(B) * H * Nk * size_t(d) * 2;
+    const size_t l_bytes = size_t(B) * H * Nq * 4;
+    const struct { const void* p; size_t n; } ins[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
+    const struct { const void* p; size_t n; } outs[] = {{o, q_bytes}, {lse, l_bytes}, {ws, w_bytes}};
+    for (const auto& w : outs) {
+        if (!w.n) continue;
+        for (const auto& r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA2_ERR_INVALID_ARG;
+        for (const auto& w2 : outs)
+            if (&w2 != &w && w2.n && overlaps(w.p, w.n, w2.p, w2.n)) return FA2_ERR_INVALID_ARG;
+    }
+    return launch_status(fa2::launch_splitkv(q, k, v, o, lse, w_bytes ? ws : nullptr, B * H, Nq, Nk,
+                                             d, scale, plan, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa2_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                             int n_parts, int rows, int d, void* stream) {
+    if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_INVALID_ARG;
+    if (n_parts < 1 || rows < 1 || int64_t(n_parts) * rows > INT32_MAX) return FA2_ERR_INVALID_ARG;
+    if (d != 32 && d != 64 && d != 96 && d != 128) return FA2_ERR_UNSUPPORTED;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(o_parts) |
+                           reinterpret_cast<uintptr_t>(lse_parts) |
+                           reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(lse);
+    if (bits & 15u) return FA2_ERR_MISALIGNED;
+    const size_t op_bytes = size_t(n_parts) * rows * size_t(d) * 4;
+    const size_t lp_bytes = size_t(n_parts) * rows * 4;
+    const size_t o_bytes = size_t(rows) * d * 2;
+    const size_t l_bytes = size_t(rows) * 4;
+    for (const auto& w : {std::make_pair(static_cast<const void*>(o), o_bytes),
+                          std::make_pair(static_cast<const void*>(lse), l_bytes)}) {
+        if (overlaps(w.first, w.second, o_parts, op_bytes) ||
+            overlaps(w.first, w.second, lse_parts, lp_bytes))
+            return FA2_ERR_INVALID_ARG;
+    }
+    if (overlaps(o, o_bytes, lse, l_bytes)) return FA2_ERR_INVALID_ARG;
+    return launch_status(fa2::launch_lse_merge(o_parts, lse_parts, o, lse, n_parts, rows, d,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 extern "C" const char* fa2_status_string(int status) {

@@ -140,6 +140,66 @@ int fa1_fwd(const void* q, const void* k, const void* v, void* o, float* lse, vo
 /* Workspace bytes fa1_fwd needs: B * H * N * (d + 2) * 4 (0 for bad sizes). */
 size_t fa1_workspace_bytes(int B, int H, int N, int d);
 
+/*
+ * fa2_fwd_splitkv -- attention of a short query block over a long key/value
+ * set (decoding), with the keys split across workgroups; non-causal.
+ *
+ *     O = softmax(scale * Q K^T) V,  LSE = natural log-sum-exp per query row,
+ *
+ * for q [B, H, Nq, d] against k, v [B, H, Nk, d].  The keys are split into
+ * ranges; each range leaves a partial result normalised over its keys with
+ * its own LSE, and the parts are merged with
+ * LSE = M + ln sum_s exp(LSE_s - M), O = sum_s exp(LSE_s - LSE) O_s -- the
+ * online-softmax recurrence over whole parts ("3.6 Attention I -- the
+ * memory problem and FlashAttention principles", 3.6.4; 3.6.9 and 3.6.10
+ * name split-key decoding without its steps).
+ *
+ *   q       : device pointer, fp16 [B, H, Nq, d]; k, v : fp16 [B, H, Nk, d].
+ *   o, lse  : device pointers, fp16 [B, H, Nq, d] and fp32 [B, H, Nq].
+ *   ws      : device pointer, caller-owned workspace of at least
+ *             fa2_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits) bytes
+ *             (fp32 partial outputs and LSEs); may be NULL when that is 0
+ *             (a single range).  ws_bytes is its size.
+ *   Nq, Nk  : >= 1, each <= 2^22, N * d <= 2^29 for both.
+ *   d       : 32, 64, 96 or 128.
+ *   n_splits: requested number of key ranges, 1 .. 4096, or 0 to let the
+ *             library choose for the shape; fa2_splitkv_splits returns the
+ *             count actually used (never an empty range).
+ *   scale, stream : as for fa2_fwd.
+ * Errors as for fa2_fwd; a missing or too small workspace, or any overlap of
+ * o, lse, ws with an input or each other, is FA2_ERR_INVALID_ARG.
+ */
+int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* ws, size_t ws_bytes, int B, int H, int Nq, int Nk, int d,
+                    float scale, int n_splits, void* stream);
+
+/* Key ranges fa2_fwd_splitkv uses for these sizes (0 for invalid sizes). */
+int fa2_splitkv_splits(int B, int H, int Nq, int Nk, int d, int n_splits);
+
+/* Workspace bytes fa2_fwd_splitkv needs: splits * B * H * Nq * (d + 1) * 4
+ * when it uses more than one range, else 0 (also 0 for invalid sizes). */
+size_t fa2_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int n_splits);
+
+/*
+ * fa2_lse_merge -- merge n_parts partial attention results over disjoint key
+ * sets (the second step of fa2_fwd_splitkv, and the merge of attention
+ * computed on key shards elsewhere, e.g. one shard per GPU).
+ *
+ *   o_parts   : device pointer, fp32 [n_parts, rows, d]: each part's output,
+ *               normalised over its own keys.
+ *   lse_parts : device pointer, fp32 [n_parts, rows]: each part's natural
+ *               log-sum-exp; -inf marks an empty part (its o_parts ignored).
+ *   o, lse    : device pointers, fp16 [rows, d] and fp32 [rows]: the merged
+ *               result, LSE = M + ln sum_s exp(LSE_s - M), O = sum_s
+ *               exp(LSE_s - LSE) O_s (rows whose parts are all empty: O = 0,
+ *               LSE = -inf).
+ *   n_parts, rows >= 1, n_parts * rows <= 2^31 - 1; d : 32, 64, 96 or 128.
+ * Errors as for fa2_fwd; o or lse overlapping an input or each other is
+ * FA2_ERR_INVALID_ARG.
+ */
+int fa2_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                  int n_parts, int rows, int d, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa2_status_string(int status);
 

@@ -195,3 +195,66 @@ def test_fa1_workspace_size():
     (dict(scale=math.nan), "FA2_ERR_INVALID_ARG")])
 def test_fa1_rejects(lib, kw, status):
     assert fcall(**kw) == getattr(fa2, status)
+
+
+# --------------------------------------------------- fa2_fwd_splitkv / merge
+@pytest.mark.parametrize("B,H,Nq,Nk,d,req", [(1, 32, 1, 65536, 128, 0), (1, 1, 1, 100, 64, 3),
+                                             (2, 3, 5, 1000, 64, 7), (1, 2, 3, 640, 32, 6),
+                                             (4, 32, 1, 4096, 64, 0), (1, 1, 200, 64, 96, 0),
+                                             (1, 1, 1, 1, 128, 0), (1, 4, 7, 5000, 128, 4096)])
+def test_split_plan_has_no_empty_range(lib, B, H, Nq, Nk, d, req):
+    n = fa2.fa2_splitkv_splits(B, H, Nq, Nk, d, req)
+    tiles = -(-Nk // 64)
+    assert 1 <= n <= tiles
+    if req:
+        assert n <= req
+    tps = -(-tiles // n)
+    assert (n - 1) * tps < tiles <= n * tps
+    ws = fa2.fa2_splitkv_workspace_bytes(B, H, Nq, Nk, d, req)
+    assert ws == (0 if n == 1 else n * B * H * Nq * (d + 1) * 4)
+
+
+def test_split_plan_auto_fills_the_chip():
+    # one query row per head, 32 heads, 64K keys: 16 ranges of 64 tiles
+    assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, 0) == 16
+    assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, 1) == 1
+    assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, -1) == 0
+
+
+def scall(q=Q, k=K, v=V, o=O, lse=L, ws=WS, ws_bytes=None, B=1, H=2, Nq=3, Nk=1000, d=64,
+          scale=0.125, n_splits=4):
+    if ws_bytes is None:
+        ws_bytes = fa2.fa2_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits)
+    return fa2.fa2_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d, scale, n_splits, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), "FA2_ERR_INVALID_ARG"), (dict(Nq=0), "FA2_ERR_INVALID_ARG"),
+    (dict(Nk=0), "FA2_ERR_INVALID_ARG"), (dict(Nk=(1 << 22) + 1), "FA2_ERR_INVALID_ARG"),
+    (dict(d=256), "FA2_ERR_UNSUPPORTED"), (dict(d=48), "FA2_ERR_UNSUPPORTED"),
+    (dict(n_splits=-1), "FA2_ERR_INVALID_ARG"), (dict(n_splits=5000), "FA2_ERR_INVALID_ARG"),
+    (dict(scale=math.inf), "FA2_ERR_INVALID_ARG"), (dict(ws=0), "FA2_ERR_INVALID_ARG"),
+    (dict(ws_bytes=64), "FA2_ERR_INVALID_ARG"), (dict(ws=WS + 8), "FA2_ERR_MISALIGNED"),
+    (dict(o=Q + 16), "FA2_ERR_INVALID_ARG"), (dict(ws=K + 16), "FA2_ERR_INVALID_ARG"),
+    (dict(lse=O + 16), "FA2_ERR_INVALID_ARG")])
+def test_splitkv_rejects(lib, kw, status):
+    assert scall(**kw) == getattr(fa2, status)
+
+
+def test_splitkv_single_range_needs_no_workspace(lib):
+    # one range: ws may be NULL; a misaligned q proves the call got past the
+    # workspace rules without reaching HIP
+    assert fa2.fa2_splitkv_workspace_bytes(1, 2, 3, 1000, 64, 1) == 0
+    assert scall(ws=0, ws_bytes=0, n_splits=1, q=Q + 2) == fa2.FA2_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(op=0), "FA2_ERR_INVALID_ARG"), (dict(n=0), "FA2_ERR_INVALID_ARG"),
+    (dict(rows=0), "FA2_ERR_INVALID_ARG"), (dict(d=256), "FA2_ERR_UNSUPPORTED"),
+    (dict(o=Q + 8), "FA2_ERR_MISALIGNED"), (dict(o=Q + 16), "FA2_ERR_INVALID_ARG"),
+    (dict(lse=K + 16), "FA2_ERR_INVALID_ARG"), (dict(lse=O + 16), "FA2_ERR_INVALID_ARG")])
+def test_lse_merge_rejects(lib, kw, status):
+    a = dict(op=Q, lp=K, o=O, lse=L, n=4, rows=100, d=64)
+    a.update(kw)
+    assert fa2.fa2_lse_merge(a["op"], a["lp"], a["o"], a["lse"], a["n"], a["rows"], a["d"], 0) == \
+        getattr(fa2, status)
