@@ -30,6 +30,11 @@ upstream gradient; FLOPs = 10*B*H*N^2*d (five products of 2*N^2*d: S, dP,
 dV, dK, dQ; halved when causal), the roofline unit is the whole call, and
 the CPU baseline is the float64 gradient oracle.
 
+A decoding workload (Nq query rows against N keys, e.g. decode_64k) is
+timed through fa2_fwd_splitkv with the library's split count: value and
+roofline are HBM GB/s of algorithmic bytes (Q, K, V read once, O and LSE
+written once) against 8 TB/s, parity is every row against the oracle.
+
 --impl fa1 times the FlashAttention-1-order comparator (fa1_fwd, d = 64)
 on the workload instead of fa2_fwd.  --batch-sweep times both, causal and
 not, at [B, 32, 2048, 64] for B = 1, 2, 4, 8, 16 (the batch experiment of
@@ -52,6 +57,8 @@ if ROOT not in sys.path:
 
 METRIC = "FA2 fwd TFLOP/s and % of MI355X fp16 MFMA peak, [4,32,2048,64]"
 METRIC_BWD = "FA2 bwd TFLOP/s and % of MI355X fp16 MFMA peak"
+METRIC_DECODE = "FA2 split-KV decode HBM GB/s (Q, K, V read, O, LSE written) and % of MI355X HBM peak"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_fwd_amd", "csrc", f)
                   for f in ("fa2_fwd_gfx950.hip", "fa2_bwd_gfx950.hip", "fa1_fwd_gfx950.hip",
@@ -216,6 +223,87 @@ def batch_sweep(torch, fa2):
     return points
 
 
+def bench_decode(args, w, torch, fa2):
+    """A decoding workload through the split key/value path; prints one JSON line."""
+    import numpy as np
+
+    from exact_attention_fwd_amd.workloads import make_decode_inputs
+    from oracle import attention_fp64
+
+    log(f"[bench] decode workload {w.name} B={w.B} H={w.H} Nq={w.nq} Nk={w.N} d={w.d}")
+    q, k, v = make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=dev)
+    n_splits = fa2.fa2_splitkv_splits(w.B, w.H, w.nq, w.N, w.d, 0)
+    ws_bytes = fa2.fa2_splitkv_workspace_bytes(w.B, w.H, w.nq, w.N, w.d, 0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    a = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+         ws_bytes, w.B, w.H, w.nq, w.N, w.d, w.scale, 0, stream.cuda_stream)
+
+    def step():
+        if fa2.fa2_fwd_splitkv(*a) != fa2.FA2_OK:
+            raise RuntimeError("fa2_fwd_splitkv failed")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+
+    def timed():
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+    steps, warmup, sec = time_calls(step, lambda: torch.cuda.synchronize(dev), args.warmup, args.steps)
+    args.steps, args.warmup = steps, warmup
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    timed()
+    torch.cuda.synchronize(dev)
+    wall = (time.perf_counter() - t0) / steps
+    ev_ms = ev0.elapsed_time(ev1) / steps
+    byt = w.hbm_bytes()
+    value = byt / wall / 1e9
+    achieved = byt / (ev_ms * 1e-3) / 1e9
+    log(f"[bench] {steps} calls ({n_splits} key ranges): wall {wall * 1e3:.4f} ms/call, events "
+        f"{ev_ms:.4f} ms, {value:.0f} GB/s ({100 * value / PEAK_HBM_GBS:.1f}% of HBM peak)")
+    result = {
+        "metric": METRIC_DECODE, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} [B={w.B},H={w.H},Nq={w.nq},Nk={w.N},d={w.d}] non-causal "
+                               f"fp16, N(0,{w.sigma:g}^2) inputs, {n_splits} key ranges",
+                   "B": w.B, "H": w.H, "Nq": w.nq, "Nk": w.N, "d": w.d, "causal": False,
+                   "n_splits": n_splits, "global_batch": w.B, "seq_len": w.N,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(f"decode:{w.name}"),
+                     "launch_ms": round(ev_ms, 5)},
+    }
+    if not args.no_parity:
+        o_ref, l_ref = attention_fp64(q, k, v, w.scale)
+        d_o = np.abs(out.cpu().numpy().astype(np.float64) - o_ref)
+        d_l = np.abs(lse.cpu().numpy().astype(np.float64) - l_ref) / np.maximum(np.abs(l_ref), 1)
+        result["parity"] = {"rows": int(w.B * w.H * w.nq), "max_abs_dO": float(d_o.max()),
+                            "mean_abs_dO": float(d_o.mean()), "max_rel_dLSE": float(d_l.max()),
+                            "pass": bool(d_o.max() <= 4e-3 and d_o.mean() <= 5e-4 and d_l.max() <= 1e-4)}
+        log(f"[bench] parity {result['parity']}")
+    if args.no_cpu_baseline:
+        result["cpu_baseline"] = None
+    else:
+        from oracle.attention import oracle_threads
+        t0 = time.perf_counter()
+        attention_fp64(q, k, v, w.scale, threads=oracle_threads())
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": byt / dt / 1e9, "unit": "GB/s", "cores": oracle_threads(),
+                                  "kind": "oracle", "sample": f"every row of {w.name}",
+                                  "seconds": round(dt, 3)}
+        log(f"[bench] cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +353,8 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if w.Nq:
+        return bench_decode(args, w, torch, fa2)
     log(f"[bench] workload {w.name} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
     q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.sigma, w.seed)
     dev = torch.device("cuda:0")

@@ -309,9 +309,11 @@ SplitPlan plan_splits(int BH, int Nq, int Nk, int requested) {
     const int n_qt = (Nq + kQW - 1) / kQW;
     int n = requested;
     if (n <= 0) {
-        // About two workgroups per CU over 256 CUs, while every split keeps
-        // at least one 64-key tile per wave (four).
-        const long target = 512;
+        // One workgroup per CU (256): measured best for d = 64 and 128 at
+        // 32..256 heads and 8K..128K keys -- every workgroup does the same
+        // work, so a second round only adds a tail.  Every split keeps at
+        // least one 64-key tile per wave (four).
+        const long target = 256;
         const long groups = long(BH) * n_qt;
         n = int(std::min<long>((target + groups - 1) / groups, std::max(1, n_tk / 4)));
     }

@@ -10,7 +10,10 @@ FlashAttention 1 and 2 forward in Triton", section on the reference shape),
 and the CuTe write-up covers head dims 64 and 128 with sequences up to 64K
 ("FlashAttention-2 from scratch in CuTe", summary).  Head dims 32, 96 and 256
 (the Triton page's remark on head dims above 128, the CuTe write-up's notes
-on 32 and 96) run the reference shape, with 16 heads at d = 256.  No public dataset is
+on 32 and 96) run the reference shape, with 16 heads at d = 256.  The
+decoding workloads (one query row per head against 64K or 8K cached keys)
+stand for the short-query case the textbook chapter points to for split
+key/value decoding; their Q is drawn with the seed, K and V with seed + 1.  No public dataset is
 involved: every tensor is i.i.d. Gaussian, drawn as float32 with numpy's
 PCG64 generator, scaled by sigma and rounded to fp16 (round-to-nearest-even).
 Draw order is Q, then K, then V from one generator seeded with ``seed``.
@@ -22,7 +25,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_rows", "stress_inputs"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_decode_inputs", "sample_rows",
+           "stress_inputs"]
 
 
 @dataclass(frozen=True)
@@ -36,6 +40,7 @@ class Workload:
     sigma: float          # standard deviation of every Q, K, V element
     seed: int = 0
     sampled_rows: int = 0  # 0: every query row is checked; else rows per (b, h)
+    Nq: int = 0            # query rows when they differ from N (N = keys); 0: Nq = N
 
     @property
     def scale(self) -> float:
@@ -45,10 +50,19 @@ class Workload:
     def shape(self):
         return (self.B, self.H, self.N, self.d)
 
+    @property
+    def nq(self) -> int:
+        return self.Nq or self.N
+
     def flops(self) -> float:
-        """4*B*H*N^2*d (two GEMMs of 2*N^2*d each per head), halved if causal."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        """4*B*H*Nq*N*d (two GEMMs of 2*Nq*N*d each per head), halved if causal."""
+        f = 4.0 * self.B * self.H * self.nq * self.N * self.d
         return f / 2 if self.causal else f
+
+    def hbm_bytes(self) -> float:
+        """Algorithmic HBM bytes: Q, K, V read once, O written once (fp16),
+        LSE written (fp32)."""
+        return self.B * self.H * (2.0 * self.d * (2 * self.nq + 2 * self.N) + 4.0 * self.nq)
 
 
 WORKLOADS = {
@@ -67,8 +81,20 @@ WORKLOADS = {
         Workload("hd96", 4, 32, 2048, 96, False, 1.0, sampled_rows=512),
         Workload("hd256", 4, 16, 2048, 256, False, 1.0, sampled_rows=512),
         Workload("hd256_causal", 4, 16, 2048, 256, True, 1.0, sampled_rows=512),
+        # decoding: one new query row per head against a long key/value cache
+        # (split key/value path; N counts the keys)
+        Workload("decode_64k", 1, 32, 65536, 128, False, 1.0, Nq=1),
+        Workload("decode_b8_8k", 8, 32, 8192, 128, False, 1.0, Nq=1),
     ]
 }
+
+
+def make_decode_inputs(w):
+    """Q [B, H, Nq, d] and K, V [B, H, N, d] of a decoding workload: Q drawn
+    with ``seed``, K and V with ``seed + 1`` (each as ``make_qkv``)."""
+    q = make_qkv(w.B, w.H, w.nq, w.d, w.sigma, w.seed)[0]
+    _, k, v = make_qkv(w.B, w.H, w.N, w.d, w.sigma, w.seed + 1)
+    return q, k, v
 
 
 def make_qkv(B, H, N, d, sigma=1.0, seed=0):

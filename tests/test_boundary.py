@@ -215,8 +215,11 @@ def test_split_plan_has_no_empty_range(lib, B, H, Nq, Nk, d, req):
 
 
 def test_split_plan_auto_fills_the_chip():
-    # one query row per head, 32 heads, 64K keys: 16 ranges of 64 tiles
-    assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, 0) == 16
+    # one query row per head, 32 heads, 64K keys: 8 ranges of 128 tiles, so
+    # 256 workgroups (one per CU); 256 heads need no split
+    assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, 0) == 8
+    assert fa2.fa2_splitkv_splits(8, 32, 1, 8192, 128, 0) == 1
+    assert fa2.fa2_splitkv_splits(1, 8, 1, 131072, 128, 0) == 32
     assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, 1) == 1
     assert fa2.fa2_splitkv_splits(1, 32, 1, 65536, 128, -1) == 0
 
