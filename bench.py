@@ -60,10 +60,18 @@ METRIC_BWD = "FA2 bwd TFLOP/s and % of MI355X fp16 MFMA peak"
 METRIC_DECODE = "FA2 split-KV decode HBM GB/s (Q, K, V read, O, LSE written) and % of MI355X HBM peak"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_fwd_amd", "csrc", f)
-                  for f in ("fa2_fwd_gfx950.hip", "fa2_bwd_gfx950.hip", "fa1_fwd_gfx950.hip",
-                            "fa2_device.h", "fa2_api.cpp",
-                            "fa2_launch.h")]
+_CSRC = os.path.join(ROOT, "exact_attention_fwd_amd", "csrc")
+# The device sources of each measured path: its HBM counters stay valid while
+# these are unchanged.
+KERNEL_SOURCES = {
+    "fwd": [os.path.join(_CSRC, f) for f in ("fa2_fwd_gfx950.hip", "fa2_device.h")],
+    "bwd": [os.path.join(_CSRC, f) for f in ("fa2_bwd_gfx950.hip", "fa2_device.h")],
+    "fa1": [os.path.join(_CSRC, f) for f in ("fa1_fwd_gfx950.hip", "fa2_device.h")],
+    "decode": [os.path.join(_CSRC, f) for f in ("fa2_splitkv_gfx950.hip", "fa2_device.h")],
+}
+# rocprofv3 kernel-name fragments of each path (a call may launch several).
+KERNEL_NAMES = {"fwd": ("fa2_fwd_kernel",), "bwd": ("fa2_bwd_dq_kernel", "fa2_bwd_dkdv_kernel"),
+                "fa1": ("fa1_fwd_kernel",), "decode": ("splitkv_partial_kernel", "lse_merge_kernel")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -71,26 +79,91 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
+def kernel_sha(path: str = "fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[path]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source."""
+def traffic_key(path: str, workload: str) -> str:
+    return workload if path == "fwd" else f"{path}:{workload}"
+
+
+def measured_traffic(path: str, workload: str):
+    """HBM bytes per call from the committed counter summary, if they were
+    taken on the current source of that path's kernels."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256") != kernel_sha():
+    w = t.get("workloads", {}).get(traffic_key(path, workload))
+    if w is None or w.get("kernel_sha256") != kernel_sha(path):
         return None
-    w = t.get("workloads", {}).get(workload)
-    return None if w is None else w.get("hbm_bytes_per_launch")
+    return w.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(path: str, w) -> float:
+    """HBM bytes a call must move at least: inputs read once, outputs written
+    once (workspaces excluded)."""
+    if path == "bwd":   # q, k, v, o, dO, LSE in; dQ, dK, dV out
+        return w.B * w.H * w.N * (16.0 * w.d + 4)
+    return w.hbm_bytes()
+
+
+def summarize_counters(directory: str) -> dict:
+    """profiles/traffic.json from rocprofv3 --pmc runs laid out as
+    <dir>/copy_<C>/ (bench.py --copy-calibration 512) and
+    <dir>/pmc_<path>_<workload>_<C>/ (bench.py --pass/--impl/--workload),
+    C in FETCH_SIZE, WRITE_SIZE.  Each counter is scaled by the factor that
+    makes it read the true bytes of the plain copy; a call's bytes are the
+    sums over its kernels of the median per-dispatch values."""
+    import csv
+    import glob
+    import statistics
+
+    from exact_attention_fwd_amd.workloads import WORKLOADS
+
+    def values(sub, names):
+        out = {}
+        for f in glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    for n in names:
+                        if n in r["Kernel_Name"]:
+                            out.setdefault(n, []).append(float(r["Counter_Value"]))
+        return out
+
+    copy_kib = 512 * 1024
+    cf = statistics.median(values("copy_FETCH_SIZE", ("copyBuffer",))["copyBuffer"])
+    cw = statistics.median(values("copy_WRITE_SIZE", ("copyBuffer",))["copyBuffer"])
+    ff, wf = copy_kib / cf, copy_kib / cw
+    res = {"note": "HBM bytes per call from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, "
+                   "median over dispatches, summed over the kernels of one call), each scaled by the "
+                   "factor that makes the same counter read the true bytes of a plain 512 MiB device "
+                   "copy (bench.py --copy-calibration 512).  An entry is valid only while the sha256 "
+                   "of its path's kernel sources matches.",
+           "calibration": {"copy_bytes": copy_kib * 1024, "fetch_size_kib": cf, "write_size_kib": cw,
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "workloads": {}}
+    for d in sorted(glob.glob(os.path.join(directory, "pmc_*_FETCH_SIZE"))):
+        stem = os.path.basename(d)[len("pmc_"):-len("_FETCH_SIZE")]
+        path, wname = stem.split("_", 1)
+        names = KERNEL_NAMES[path]
+        fv = values(f"pmc_{stem}_FETCH_SIZE", names)
+        wv = values(f"pmc_{stem}_WRITE_SIZE", names)
+        fk = sum(statistics.median(v) for v in fv.values())
+        wk = sum(statistics.median(v) for v in wv.values())
+        rd, wr = fk * 1024 * ff, wk * 1024 * wf
+        alg = algorithmic_bytes(path, WORKLOADS[wname])
+        res["workloads"][traffic_key(path, wname)] = {
+            "kernel_sha256": kernel_sha(path), "kernels": sorted(fv), "fetch_size_kib": fk,
+            "write_size_kib": wk, "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr),
+            "hbm_bytes_per_launch": int(rd + wr), "algorithmic_bytes": int(alg),
+            "ratio_to_algorithmic": round((rd + wr) / alg, 4)}
+    return res
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -279,7 +352,7 @@ def bench_decode(args, w, torch, fa2):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(f"decode:{w.name}"),
+                     "traffic": measured_traffic("decode", w.name),
                      "launch_ms": round(ev_ms, 5)},
     }
     if not args.no_parity:
@@ -319,10 +392,21 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="instead: build profiles/traffic.json from rocprofv3 --pmc runs in DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        res = summarize_counters(args.summarize_counters)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+        for k, v in res["workloads"].items():
+            log(f"[counters] {k}: {v['hbm_bytes_per_launch'] / 1e6:.2f} MB per call, "
+                f"{v['ratio_to_algorithmic']}x algorithmic")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the attention forward of one "
@@ -449,8 +533,8 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_FP16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name if args.which == "fwd" and args.impl == "fa2"
-                                                 else f"{args.which}-{args.impl}:{w.name}"),
+                     "traffic": measured_traffic(
+                         "bwd" if args.which == "bwd" else args.impl.replace("fa2", "fwd"), w.name),
                      "launch_ms": round(ev_ms, 5)},
     }
 
