@@ -36,6 +36,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "fa2_device.h"
 #include "fa2_launch.h"
@@ -51,6 +52,8 @@ struct BwdCfg {
     static constexpr int kWaves = 4;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kRows = kWaves * kQW;         // queries (dQ) or keys (dK, dV) per workgroup
+    // (D = 128 uses the software-pipelined dK/dV kernel below; measured 13-18 %
+    // faster there, and slower at D = 96, where two waves share each SIMD.)
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = D / 8;              // 16-byte chunks per row
     static constexpr int kTileBytes = kBK * kRowBytes;
@@ -374,6 +377,277 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
     store_rows<D>(make_rsrc(dV + head, head_bytes), my_k, hi, dv, 1.0f);
 }
 
+// ------------------------------------------------- dK, dV, software-pipelined
+// At D = 128 the dK/dV kernel runs one wave per SIMD (its registers need a
+// whole SIMD), so nothing hides one wave's VALU work behind another wave's
+// MFMAs.  This variant pipelines it inside the wave, over 32-query blocks j:
+// step j issues the dV/dK products of block j-1 and the S/dP products of
+// block j+1 (independent of block j's softmax) slot by slot, with the P / dS
+// arithmetic of block j spread between them.  S, dP, P and dS are
+// double-buffered by block parity.  Query tiles (64 rows = 2 blocks) rotate
+// through three LDS buffers: the tile read by block j-1's products is free
+// after even step 2i, tile i+2 is stored during odd step 2i+1 and read from
+// step 2i+3 on, so one barrier after every even step covers both hazards.
+constexpr int kRing = 5;   // LDS operand reads run kRing - 1 products ahead
+
+template <int D>
+struct KvStream {
+    using B = BwdCfg<D>;
+    static constexpr int kPV = 4 * B::kDBlocks;   // dV and dK products of a block
+    static constexpr int kQK = 2 * B::kDSteps;    // S and dP products of a block
+    static constexpr int kSlots = kPV + kQK;
+    static constexpr int kTile = kBK * B::kRowBytes;
+    // Element pairs (2 of the 16 per lane) enter the three-stage VALU chain
+    // (argument, exp2, dS and fp16 packing) in slots [0, kSlots - 2).
+    static constexpr int pair_begin(int q) { return (q * (kSlots - 2)) / 8; }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdCfg<D>::kThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
+                                const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
+                                const float* __restrict__ LSE, const float* __restrict__ Delta,
+                                _Float16* __restrict__ dK, _Float16* __restrict__ dV, int N,
+                                int n_ktiles, int n_wg, float c2, float sigma) {
+    using C = BwdCfg<D>;
+    using S = KvStream<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char qbuf[3][S::kTile];
+    __shared__ __attribute__((aligned(16))) unsigned char obuf[3][S::kTile];
+    __shared__ __attribute__((aligned(16))) float lbuf[3][kBK], dbuf[3][kBK];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int logical = xcd_logical_id(blockIdx.x, n_wg);
+    const int bh = __builtin_amdgcn_readfirstlane(logical / n_ktiles);
+    const int kt = __builtin_amdgcn_readfirstlane(logical - bh * n_ktiles);
+    const int k0 = kt * C::kRows;
+    const size_t head = size_t(bh) * size_t(N) * D;
+    const uint32_t head_bytes = uint32_t(N) * C::kRowBytes;
+    const auto rQ = make_rsrc(Q + head, head_bytes);
+    const auto rK = make_rsrc(K + head, head_bytes);
+    const auto rV = make_rsrc(V + head, head_bytes);
+    const auto rdO = make_rsrc(dO + head, head_bytes);
+    const auto rL = make_rsrc(LSE + size_t(bh) * N, uint32_t(N) * 4);
+    const auto rD = make_rsrc(Delta + size_t(bh) * N, uint32_t(N) * 4);
+    const int kw0 = k0 + wave * kQW;       // first key of this wave
+    const int my_k = kw0 + l32;
+
+    h8 kf[C::kDSteps], vf[C::kDSteps];
+#pragma unroll
+    for (int ds = 0; ds < C::kDSteps; ++ds) {
+        const int off = my_k * C::kRowBytes + 32 * ds + 16 * hi;
+        kf[ds] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0));
+        vf[ds] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0));
+    }
+
+    const int n_qt = (N + kBK - 1) / kBK;
+    const int t0 = CAUSAL ? k0 / kBK : 0;        // first query tile that sees these keys
+    const int nb = 2 * (n_qt - t0);              // 32-query blocks to walk
+
+    // Staging of query tile t: chunks wave + kWaves*j of row `lane`, plus the
+    // row's log2-domain LSE (wave 0) and delta (wave 1).
+    u32x4 sq[C::kStage], so[C::kStage];
+    float sl = 0.f, sd = 0.f;
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            const int off = (t * kBK + lane) * C::kRowBytes + (wave + C::kWaves * j) * 16;
+            sq[j] = __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0);
+            so[j] = __builtin_amdgcn_raw_buffer_load_b128(rdO, off, 0, 0);
+        }
+        if (wave == 0) sl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (t * kBK + lane) * 4, 0, 0)) * kLog2e;
+        if (wave == 1) sd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (t * kBK + lane) * 4, 0, 0));
+    };
+    auto put = [&](int b) {
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            const int ch = wave + C::kWaves * j;
+            *reinterpret_cast<u32x4*>(&qbuf[b][0] + lds_v_off(ch, lane)) = sq[j];
+            *reinterpret_cast<u32x4*>(&obuf[b][0] + lds_v_off(ch, lane)) = so[j];
+        }
+        if (wave == 0) lbuf[b][lane] = sl;
+        if (wave == 1) dbuf[b][lane] = sd;
+    };
+    const SwBase sw(lane);
+    const TrBase tr(lane);
+
+    f32x16 dk[C::kDBlocks], dv[C::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < C::kDBlocks; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+    f32x16 s_[2], dp_[2];       // S and dP of the blocks of parity 0 / 1
+    h8 pf[2][2], dsf[2][2];     // fp16 P and dS of the blocks of parity 0 / 1
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        pf[i][0] = pf[i][1] = dsf[i][0] = dsf[i][1] = h8{};
+    }
+
+    // Prologue: tiles t0 and t0+1 to LDS buffers 0 and 1; S and dP of block 0.
+    fetch(t0);
+    put(0);
+    fetch(t0 + 1);
+    put(1);
+    __syncthreads();
+    {
+        f32x16 a = f32x16{}, b = f32x16{};
+#pragma unroll
+        for (int ds = 0; ds < C::kDSteps; ++ds) {
+            a = mfma(*reinterpret_cast<const h8*>(&qbuf[0][0] + sw.b[ds & 1] + sw_imm(ds, 0)), kf[ds], a);
+            b = mfma(*reinterpret_cast<const h8*>(&obuf[0][0] + sw.b[ds & 1] + sw_imm(ds, 0)), vf[ds], b);
+        }
+        s_[0] = a;
+        dp_[0] = b;
+    }
+
+    // Step j (PAR = j & 1): products of block j-1 (dV, dK) and j+1 (S, dP),
+    // softmax-side arithmetic of block j.
+    auto step = [&](auto par_tag, int j) {
+        constexpr int PAR = decltype(par_tag)::value;
+        const int ti = j >> 1;                          // tile of block j, relative to t0
+        // block j-1's tile; for j = 0 (no such block, P = dS = 0) tile 0,
+        // whose contents are finite
+        const int prev_buf = (j > 0 ? (j - 1) >> 1 : 0) % 3;
+        const unsigned char* qb_prev = &qbuf[prev_buf][0];
+        const unsigned char* ob_prev = &obuf[prev_buf][0];
+        const unsigned char* qb_next = &qbuf[((j + 1) >> 1) % 3][0];
+        const unsigned char* ob_next = &obuf[((j + 1) >> 1) % 3][0];
+        const float* lb = &lbuf[ti % 3][0];
+        const float* dlb = &dbuf[ti % 3][0];
+        constexpr int PREV = 1 - PAR;                  // parity of blocks j-1 and j+1
+        // Row statistics of block j's 16 query rows of this lane (register r =
+        // 4g + k: row 32*PAR + 8g + 4*hi + k of the tile).
+        float Lr[16], Dr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 L = *reinterpret_cast<const float4*>(lb + 32 * PAR + 8 * g + 4 * hi);
+            const float4 Dv = *reinterpret_cast<const float4*>(dlb + 32 * PAR + 8 * g + 4 * hi);
+            Lr[4 * g] = L.x; Lr[4 * g + 1] = L.y; Lr[4 * g + 2] = L.z; Lr[4 * g + 3] = L.w;
+            Dr[4 * g] = Dv.x; Dr[4 * g + 1] = Dv.y; Dr[4 * g + 2] = Dv.z; Dr[4 * g + 3] = Dv.w;
+        }
+        const int q0 = (t0 + ti) * kBK + 32 * PAR;     // first query of block j
+        const bool masked = CAUSAL && q0 < kw0 + kQW - 1;
+        // j = 0 has no block j-1: its products run on P = dS = 0 (pf / dsf of
+        // parity 1 start zeroed and are first written by block 1).
+
+        h8 ring[kRing];
+        auto read = [&](int p) {
+            if (p < S::kPV) {
+                const int kk = p / (2 * C::kDBlocks), rem = p % (2 * C::kDBlocks);
+                const int db = rem >> 1, which = rem & 1;
+                const int imm = tr_imm(2 * PREV + kk, db);
+                ring[p % kRing] = read_tr_operand(which ? qb_prev : ob_prev, tr, imm);
+            } else {
+                const int a = p - S::kPV, ds = a >> 1, which = a & 1;
+                ring[p % kRing] = *reinterpret_cast<const h8*>((which ? ob_next : qb_next) + sw.b[ds & 1] + sw_imm(ds, PREV));
+            }
+        };
+        auto job = [&](int p) {
+            const h8 a = ring[p % kRing];
+            if (p < S::kPV) {
+                const int kk = p / (2 * C::kDBlocks), rem = p % (2 * C::kDBlocks);
+                const int db = rem >> 1, which = rem & 1;
+                if (which) dk[db] = mfma(a, dsf[PREV][kk], dk[db]);
+                else dv[db] = mfma(a, pf[PREV][kk], dv[db]);
+            } else {
+                const int q = p - S::kPV, ds = q >> 1, which = q & 1;
+                if (which) dp_[PREV] = mfma(a, vf[ds], ds == 0 ? f32x16{} : dp_[PREV]);
+                else s_[PREV] = mfma(a, kf[ds], ds == 0 ? f32x16{} : s_[PREV]);
+            }
+        };
+        float arg[16], pe[16];
+        auto pb = [&](int p) {    // first pair entering at slot p or later
+            int q = 0;
+            while (q < 8 && S::pair_begin(q) < p) ++q;
+            return q;
+        };
+        auto valu = [&](int p) {
+            // stage 3: dS, fp16 P and dS of the pairs that entered two slots ago
+#pragma unroll
+            for (int q = pb(p - 2); q < pb(p - 1); ++q) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 2 * q + h;
+                    const float d_ = pe[r] * (dp_[PAR][r] - Dr[r]);
+                    pf[PAR][r >> 3][r & 7] = (_Float16)pe[r];
+                    dsf[PAR][r >> 3][r & 7] = (_Float16)d_;
+                }
+                pin(pf[PAR][q >> 2]);
+                pin(dsf[PAR][q >> 2]);
+            }
+            // stage 2: exp2, causal mask
+#pragma unroll
+            for (int q = pb(p - 1); q < pb(p); ++q) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 2 * q + h;
+                    float e = __builtin_amdgcn_exp2f(arg[r]);
+                    if (masked && my_k > q0 + 8 * (r >> 2) + 4 * hi + (r & 3)) e = 0.f;
+                    pe[r] = e;
+                    pin(pe[r]);
+                }
+            }
+            // stage 1: scaled score minus the row's log2-domain LSE
+#pragma unroll
+            for (int q = pb(p); q < pb(p + 1); ++q) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 2 * q + h;
+                    arg[r] = __builtin_fmaf(s_[PAR][r], c2, -Lr[r]);
+                    pin(arg[r]);
+                }
+            }
+        };
+        // Staging: an even step fetches tile ti+2 into registers (free since
+        // the previous odd step stored theirs); the next, odd step stores it
+        // into buffer (ti+2) % 3, whose old tile ti-1 was last read before the
+        // barrier that ends the even step.
+        if (PAR == 0) fetch(t0 + ti + 2);
+#pragma unroll
+        for (int p = 0; p < kRing - 1; ++p) read(p);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < S::kSlots; ++p) {
+            if (p + kRing - 1 < S::kSlots) read(p + kRing - 1);
+            job(p);
+            __builtin_amdgcn_sched_barrier(0);
+            valu(p);
+            if (PAR == 1 && p == S::kSlots / 2) put((ti + 2) % 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (PAR == 0) __syncthreads();
+    };
+
+    int j = 0;
+    for (; j + 1 < nb; j += 2) {
+        step(std::integral_constant<int, 0>{}, j);
+        step(std::integral_constant<int, 1>{}, j + 1);
+    }
+    // nb is even: every block has been softmax'd; block nb-1 still owes its
+    // dV / dK products.
+    {
+        const unsigned char* qb_prev = &qbuf[((nb - 1) >> 1) % 3][0];
+        const unsigned char* ob_prev = &obuf[((nb - 1) >> 1) % 3][0];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int db = 0; db < C::kDBlocks; ++db) {
+                const int imm = tr_imm(2 + kk, db);
+                dv[db] = mfma(read_tr_operand(ob_prev, tr, imm), pf[1][kk], dv[db]);
+                dk[db] = mfma(read_tr_operand(qb_prev, tr, imm), dsf[1][kk], dk[db]);
+            }
+        }
+    }
+    store_rows<D>(make_rsrc(dK + head, head_bytes), my_k, hi, dk, sigma);
+    store_rows<D>(make_rsrc(dV + head, head_bytes), my_k, hi, dv, 1.0f);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N,
@@ -390,10 +664,17 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
                        delta, N, n_tiles, n_wg, c2, sigma);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
-                       Q, K, V, dO, lse, static_cast<const float*>(delta),
-                       static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
-                       c2, sigma);
+    if constexpr (D == 128) {
+        hipLaunchKernelGGL((fa2_bwd_dkdv_stream_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0,
+                           stream, Q, K, V, dO, lse, static_cast<const float*>(delta),
+                           static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
+                           c2, sigma);
+    } else {
+        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
+                           Q, K, V, dO, lse, static_cast<const float*>(delta),
+                           static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
+                           c2, sigma);
+    }
     return hipGetLastError();
 }
 
