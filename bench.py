@@ -70,7 +70,7 @@ KERNEL_SOURCES = {
     "decode": [os.path.join(_CSRC, f) for f in ("fa2_splitkv_gfx950.hip", "fa2_device.h")],
 }
 # rocprofv3 kernel-name fragments of each path (a call may launch several).
-KERNEL_NAMES = {"fwd": ("fa2_fwd_kernel",), "bwd": ("fa2_bwd_dq_kernel", "fa2_bwd_dkdv_kernel"),
+KERNEL_NAMES = {"fwd": ("fa2_fwd_kernel",), "bwd": ("fa2_bwd_dq_kernel", "fa2_bwd_dkdv"),
                 "fa1": ("fa1_fwd_kernel",), "decode": ("splitkv_partial_kernel", "lse_merge_kernel")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -159,7 +159,8 @@ def summarize_counters(directory: str) -> dict:
         rd, wr = fk * 1024 * ff, wk * 1024 * wf
         alg = algorithmic_bytes(path, WORKLOADS[wname])
         res["workloads"][traffic_key(path, wname)] = {
-            "kernel_sha256": kernel_sha(path), "kernels": sorted(fv), "fetch_size_kib": fk,
+            "kernel_sha256": kernel_sha(path), "kernels": sorted(fv),
+            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "fetch_size_kib": fk,
             "write_size_kib": wk, "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr),
             "hbm_bytes_per_launch": int(rd + wr), "algorithmic_bytes": int(alg),
             "ratio_to_algorithmic": round((rd + wr) / alg, 4)}
@@ -400,9 +401,17 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_counters:
+        # entries from DIR replace those of the same path and workload;
+        # the others (each with its own sha256 and factors) are kept
         res = summarize_counters(args.summarize_counters)
+        try:
+            with open(TRAFFIC_FILE) as f:
+                old = json.load(f).get("workloads", {})
+        except (OSError, ValueError):
+            old = {}
+        res["workloads"] = {**old, **res["workloads"]}
         with open(TRAFFIC_FILE, "w") as f:
-            json.dump(res, f, indent=1)
+            json.dump(res, f, indent=1, sort_keys=True)
         for k, v in res["workloads"].items():
             log(f"[counters] {k}: {v['hbm_bytes_per_launch'] / 1e6:.2f} MB per call, "
                 f"{v['ratio_to_algorithmic']}x algorithmic")

@@ -82,7 +82,7 @@ def test_counter_summary_from_rocprof_csvs(tmp_path):
                 fh.write(f"{name},{val}\n")
     write("copy_FETCH_SIZE", [("__amd_rocclr_copyBuffer", 262144.0)] * 5)
     write("copy_WRITE_SIZE", [("__amd_rocclr_copyBuffer", 524288.0)] * 5)
-    write("pmc_bwd_ref_FETCH_SIZE", [("fa2_bwd_dq_kernel<64>", 100.0), ("fa2_bwd_dkdv_kernel<64>", 50.0)] * 3)
+    write("pmc_bwd_ref_FETCH_SIZE", [("fa2_bwd_dq_kernel<64>", 100.0), ("fa2_bwd_dkdv_stream_kernel<64>", 50.0)] * 3)
     write("pmc_bwd_ref_WRITE_SIZE", [("fa2_bwd_dq_kernel<64>", 10.0), ("fa2_bwd_dkdv_kernel<64>", 20.0)] * 3)
     res = bench.summarize_counters(str(tmp_path))
     assert res["calibration"]["fetch_factor"] == 2.0 and res["calibration"]["write_factor"] == 1.0
