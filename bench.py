@@ -446,6 +446,10 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if w.Nq and (args.which != "fwd" or args.impl != "fa2"):
+        ap.error(f"{w.name} is a decoding workload: it runs the split key/value forward only")
+    if args.impl == "fa1" and (args.which != "fwd" or w.d != 64):
+        ap.error("--impl fa1 is the forward comparator at head dim 64")
     if w.Nq:
         return bench_decode(args, w, torch, fa2)
     log(f"[bench] workload {w.name} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")

@@ -203,6 +203,8 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
     B, H, N, d = q.shape
     if scale is None:
         scale = d ** -0.5
+    if lse is None:
+        raise ValueError("lse must be the forward's LSE output for the same q, k, v")
     lse = _out(lse, q, torch.float32, (B, H, N), "lse")
     dq = _out(dq, q, torch.float16, q.shape, "dq")
     dk = _out(dk, q, torch.float16, q.shape, "dk")
@@ -257,7 +259,7 @@ def fwd_splitkv(q, k, v, scale=None, n_splits=0, out=None, lse=None, workspace=N
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if k.shape[:2] != q.shape[:2] or k.shape[3] != d or k.device != q.device:
-        raise ValueError("k, v must be [B, H, Nk, d] on q's device")
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d], on one device")
     if scale is None:
         scale = d ** -0.5
     out = _out(out, q, torch.float16, q.shape, "out")

@@ -21,7 +21,8 @@ bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
     return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
-// Sizes, scale and head dim shared by both entry points; 0 when valid.
+// Sizes, scale and head dim of the square-attention entry points (forward,
+// backward, FA1 order); 0 when valid.
 int check_sizes(int B, int H, int N, int d, float scale, int max_d) {
     if (B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
     // Per-head byte offsets are 32-bit buffer offsets: N * d * 2 plus a few
@@ -105,7 +106,7 @@ extern "C" int fa2_bwd(const void* q, const void* k, const void* v, const void* 
 }
 
 extern "C" size_t fa1_workspace_bytes(int B, int H, int N, int d) {
-    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    if (B < 1 || H < 1 || N < 1 || d < 1 || int64_t(B) * H * N > INT32_MAX) return 0;
     return fa2::fa1_workspace_floats(B * H, N, d) * sizeof(float);
 }
 

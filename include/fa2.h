@@ -137,7 +137,8 @@ int fa1_fwd(const void* q, const void* k, const void* v, void* o, float* lse, vo
             size_t ws_bytes, int B, int H, int N, int d, float scale, int causal,
             void* stream);
 
-/* Workspace bytes fa1_fwd needs: B * H * N * (d + 2) * 4 (0 for bad sizes). */
+/* Workspace bytes fa1_fwd needs: B * H * N * (d + 2) * 4 (0 for bad sizes,
+ * including B * H * N > 2^31 - 1). */
 size_t fa1_workspace_bytes(int B, int H, int N, int d);
 
 /*

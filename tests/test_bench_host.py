@@ -101,3 +101,13 @@ def test_committed_traffic_summary_is_well_formed():
         assert w["hbm_bytes_per_launch"] == w["hbm_read_bytes"] + w["hbm_write_bytes"], name
         assert w["ratio_to_algorithmic"] == pytest.approx(
             w["hbm_bytes_per_launch"] / w["algorithmic_bytes"], rel=1e-3), name
+
+
+@pytest.mark.parametrize("argv", [["--workload", "decode_64k", "--pass", "bwd"],
+                                  ["--workload", "decode_64k", "--impl", "fa1"],
+                                  ["--impl", "fa1", "--pass", "bwd"],
+                                  ["--impl", "fa1", "--workload", "ref_d128"]])
+def test_meaningless_flag_combinations_are_rejected(argv):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "error" in r.stderr and r.stdout == ""

@@ -261,3 +261,7 @@ def test_lse_merge_rejects(lib, kw, status):
     a.update(kw)
     assert fa2.fa2_lse_merge(a["op"], a["lp"], a["o"], a["lse"], a["n"], a["rows"], a["d"], 0) == \
         getattr(fa2, status)
+
+
+def test_fa1_workspace_size_rejects_huge_grids():
+    assert fa2.fa1_workspace_bytes(1 << 16, 1 << 16, 1, 64) == 0
