@@ -17,10 +17,12 @@
 //
 //  * Each wave owns 32 whole query rows, so every row reduction stays inside
 //    the wave.  Head dims 32, 64, 96, 128 and 256 are compiled.  A workgroup
-//    is 8 waves (256 queries of one (batch, head), one workgroup per CU) at
-//    d = 128 and 4 waves (128 queries) otherwise; two waves share each SIMD,
-//    except at d = 256, where a wave's 32x256 fp32 accumulator needs the
-//    registers of a whole SIMD.
+//    is 8 waves (256 queries of one (batch, head)) at d = 128 and at
+//    non-causal d = 64, and 4 waves (128 queries) otherwise: 8 waves halve
+//    the K/V staging per query, while under the causal mask at d = 64 the
+//    smaller group wastes fewer masked keys on the diagonal.  Two waves share
+//    each SIMD, except at d = 256, where a wave's 32x256 fp32 accumulator
+//    needs the registers of a whole SIMD.
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_f16 (A = 32 keys x 16 dims from LDS, B = Q^T held in
 //    registers for the whole loop).  In the 32x32 accumulator a lane then
@@ -89,12 +91,13 @@ using namespace dev;
 constexpr float kLazyBound = 256.0f;   // 2^kLazy, kLazy = 8
 constexpr int kAhead = 4;                // LDS operand reads in flight ahead of the MFMAs
 
-template <int D>
+template <int D, bool CAUSAL>
 struct Cfg {
-    // Waves per workgroup (see the header): 8 at d = 128, 4 otherwise.  Two
-    // waves per SIMD, except at d = 256, whose registers need a SIMD each.
+    // Waves per workgroup (see the header): 8 at d = 128 and at non-causal
+    // d = 64, 4 otherwise.  Two waves per SIMD, except at d = 256, whose
+    // registers need a SIMD each.
     static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
-    static constexpr int kWaves = D == 128 ? 8 : 4;
+    static constexpr int kWaves = (D == 128 || (D == 64 && !CAUSAL)) ? 8 : 4;
     static constexpr int kWavesPerSimd = D == 256 ? 1 : 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBQ = kWaves * kQW;               // query rows per workgroup
@@ -128,13 +131,13 @@ struct Cfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(Cfg<D>::kThreads)
-__attribute__((amdgpu_waves_per_eu(Cfg<D>::kWavesPerSimd, Cfg<D>::kWavesPerSimd)))
+__global__ __launch_bounds__((Cfg<D, CAUSAL>::kThreads))
+__attribute__((amdgpu_waves_per_eu(Cfg<D, CAUSAL>::kWavesPerSimd, Cfg<D, CAUSAL>::kWavesPerSimd)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
                     float* __restrict__ LSE, int N, int n_qtiles, int n_wg, float c,
                     uint32_t q_and, uint32_t q_xor) {
-    using C = Cfg<D>;
+    using C = Cfg<D, CAUSAL>;
     static_assert(C::schedule_ok(), "P chunk rewritten before its last reader");
     __shared__ __attribute__((aligned(16))) unsigned char kb0[C::kTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char kb1[C::kTileBytes];
@@ -455,7 +458,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                   int N, float c, uint32_t q_and, uint32_t q_xor, hipStream_t stream) {
-    using C = Cfg<D>;
+    using C = Cfg<D, CAUSAL>;
     const int n_qtiles = (N + C::kBQ - 1) / C::kBQ;
     const int n_wg = n_qtiles * BH;
     hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
