@@ -46,8 +46,9 @@
 //    rewritten only after its last reader has issued.
 //  * Lazy reference max, checked after the fact: the stream computes the
 //    weights exp2(S*c - m2) against the row's current reference m2 without a
-//    row max.  If the row's weights in the tile sum to at most 2^kLazy, each
-//    weight is at most 2^kLazy (safe in fp16) and m2 stays, alpha = 1.
+//    row max.  If every lane's 16 weights of the tile sum to at most
+//    2^kLazy, each weight is at most 2^kLazy (safe in fp16) and m2 stays,
+//    alpha = 1 (checking each lane's part needs no cross-lane step).
 //    Otherwise (a weight may exceed 2^kLazy: the row max moved up, or m2 is
 //    not finite) the wave redoes the tile with the recurrence step
 //    itself: m2 := max(m2, scaled tile max), alpha = exp2(m2_old - m2_new),
@@ -86,8 +87,8 @@ namespace {
 
 using namespace dev;
 
-// A tile keeps the row's reference max while the row's weights in it sum to
-// at most 2^kLazy, so every weight stays <= 2^8, far inside fp16 range.
+// A tile keeps the row's reference max while each lane's weights in it sum
+// to at most 2^kLazy, so every weight stays <= 2^8, far inside fp16 range.
 constexpr float kLazyBound = 256.0f;   // 2^kLazy, kLazy = 8
 constexpr int kAhead = 4;                // LDS operand reads in flight ahead of the MFMAs
 
@@ -317,7 +318,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         // Softmax of tile t against the current reference max, one slice per
         // slot; checked after the stream.
         const float shift = m2;
-        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+        float rsum[4];
         float arg[32], pe[32];
         auto sv = [&](int i) { return s_cur[i >> 4][i & 15]; };
         auto pb = [&](int p) { return p < 0 ? 0 : C::pair_begin(p); };
@@ -328,7 +329,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int e = 2 * j + h;
-                    rsum[e & 3] += pe[e];
+                    rsum[e & 3] = e < 4 ? pe[e] : rsum[e & 3] + pe[e];
                     pf[e >> 3][e & 7] = (_Float16)pe[e];
                     pin(rsum[e & 3]);
                 }
@@ -381,13 +382,13 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
-        // The tile's weights for this row sum to at most 2^kLazy: every
-        // weight is then <= 2^kLazy and the reference max stays.  Otherwise
+        // This lane's weights of the tile sum to at most 2^kLazy in every
+        // lane: each weight is then <= 2^kLazy and the reference max stays.
+        // (The first weight of each partial sum starts it, no add of 0.)  Otherwise
         // (the row max moved up, or m2 was still -inf) take the recurrence
         // step exactly: m2 := max(m2, tile max), rescale, recompute.
         const float part = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
-        const float tot = pair_sum(part);
-        if (__builtin_amdgcn_ballot_w64(!(tot <= kLazyBound))) {
+        if (__builtin_amdgcn_ballot_w64(!(part <= kLazyBound))) {
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 32; ++i) mx = __builtin_fmaxf(mx, sv(i));
