@@ -67,7 +67,7 @@
 //    stores past N are dropped by the hardware, so the tail needs no branch.
 //  * Workgroup ids are remapped so that all Q tiles of one head run on the
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2;
-//    causal grids start with the longest rows.
+//    causal grids start with the longest rows, across small groups of heads.
 
 // LDS tile layouts (fa2_device.h): K chunk-major, V swizzled (chunk-major
 // with an XOR of the row) for the transposing reads.  Both keep every
@@ -136,8 +136,8 @@ __global__ __launch_bounds__((Cfg<D, CAUSAL>::kThreads))
 __attribute__((amdgpu_waves_per_eu(Cfg<D, CAUSAL>::kWavesPerSimd, Cfg<D, CAUSAL>::kWavesPerSimd)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
-                    float* __restrict__ LSE, int N, int n_qtiles, int n_wg, float c,
-                    uint32_t q_and, uint32_t q_xor) {
+                    float* __restrict__ LSE, int N, int n_qtiles, int n_wg, int group,
+                    float c, uint32_t q_and, uint32_t q_xor) {
     using C = Cfg<D, CAUSAL>;
     static_assert(C::schedule_ok(), "P chunk rewritten before its last reader");
     __shared__ __attribute__((aligned(16))) unsigned char kb0[C::kTileBytes];
@@ -154,8 +154,21 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Logical tile id: consecutive ids (the Q tiles of one head) go to one XCD.
     const int wg = blockIdx.x;
     const int logical = xcd_logical_id(wg, n_wg);
-    const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
-    int qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
+    int bh, qt;
+    if (CAUSAL && group > 1) {
+        // Longest rows first across `group` heads at a time: consecutive ids
+        // take the same query-tile rank of the group's heads, so the
+        // workgroups an XCD runs together start with the longest tiles of a
+        // few heads (their K/V shared in L2) and the shortest come last.
+        const int g0 = logical / (group * n_qtiles);
+        const int i = logical - g0 * group * n_qtiles;
+        const int rank = i / group;
+        bh = __builtin_amdgcn_readfirstlane(g0 * group + (i - rank * group));
+        qt = __builtin_amdgcn_readfirstlane(rank);
+    } else {
+        bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
+        qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
+    }
     if (CAUSAL) qt = n_qtiles - 1 - qt;   // longest rows first
     const int q0 = qt * C::kBQ;
     const size_t head = size_t(bh) * size_t(N) * D;
@@ -462,10 +475,21 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     using C = Cfg<D, CAUSAL>;
     const int n_qtiles = (N + C::kBQ - 1) / C::kBQ;
     const int n_wg = n_qtiles * BH;
+    // Causal head groups: about as many heads' query tiles as an XCD (32 CUs)
+    // runs at once, kept whole inside each XCD's range of logical ids;
+    // halved until they fit, 1 = head by head.
+    int group = 1;
+    if (CAUSAL && n_wg % 8 == 0) {
+        const int at_once = 32 * (4 * C::kWavesPerSimd / C::kWaves);   // workgroups per XCD
+        int g = 1;
+        while (2 * g * n_qtiles <= at_once) g *= 2;
+        while (g > 1 && (n_wg / 8) % (g * n_qtiles) != 0) g /= 2;
+        group = g;
+    }
     hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                        static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
                        static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, N,
-                       n_qtiles, n_wg, c, q_and, q_xor);
+                       n_qtiles, n_wg, group, c, q_and, q_xor);
     return hipGetLastError();
 }
 
