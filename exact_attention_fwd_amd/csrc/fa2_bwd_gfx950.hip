@@ -113,7 +113,7 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
                        const _Float16* __restrict__ V, const _Float16* __restrict__ O,
                        const _Float16* __restrict__ dO, const float* __restrict__ LSE,
                        _Float16* __restrict__ dQ, float* __restrict__ Delta, int N,
-                       int n_qtiles, int n_wg, float c2, float sigma) {
+                       int n_qtiles, int n_wg, int group, float c2, float sigma) {
     using C = BwdCfg<D>;
     // K tile swizzled (plain reads for S^T, transposed reads for dQ^T), V
     // tile chunk-major (plain reads for dP^T).
@@ -129,8 +129,9 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
     const int hi = lane >> 5;
 
     const int logical = xcd_logical_id(blockIdx.x, n_wg);
-    const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
-    int qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
+    const HeadTile ht = head_tile_of(logical, n_qtiles, CAUSAL ? group : 1);   // causal: a few heads at a time
+    const int bh = ht.bh;
+    int qt = ht.rank;
     if (CAUSAL) qt = n_qtiles - 1 - qt;   // longest rows first
     const int q0 = qt * C::kRows;
     const size_t head = size_t(bh) * size_t(N) * D;
@@ -243,7 +244,7 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
                          const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
                          const float* __restrict__ LSE, const float* __restrict__ Delta,
                          _Float16* __restrict__ dK, _Float16* __restrict__ dV, int N,
-                         int n_ktiles, int n_wg, float c2, float sigma) {
+                         int n_ktiles, int n_wg, int group, float c2, float sigma) {
     using C = BwdCfg<D>;
     // Q and dO tiles swizzled (plain reads for S and dP, transposed reads for
     // dK^T and dV^T); per-query log2-domain LSE and delta beside them.
@@ -260,8 +261,9 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
     const int hi = lane >> 5;
 
     const int logical = xcd_logical_id(blockIdx.x, n_wg);
-    const int bh = __builtin_amdgcn_readfirstlane(logical / n_ktiles);
-    const int kt = __builtin_amdgcn_readfirstlane(logical - bh * n_ktiles);   // causal: tile 0 is the longest
+    const HeadTile ht = head_tile_of(logical, n_ktiles, CAUSAL ? group : 1);   // causal: tile 0 is the longest
+    const int bh = ht.bh;
+    const int kt = ht.rank;
     const int k0 = kt * C::kRows;
     const size_t head = size_t(bh) * size_t(N) * D;
     const uint32_t head_bytes = uint32_t(N) * C::kRowBytes;
@@ -411,7 +413,7 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
                                 const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
                                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                                 _Float16* __restrict__ dK, _Float16* __restrict__ dV, int N,
-                                int n_ktiles, int n_wg, float c2, float sigma) {
+                                int n_ktiles, int n_wg, int group, float c2, float sigma) {
     using C = BwdCfg<D>;
     using S = KvStream<D>;
     __shared__ __attribute__((aligned(16))) unsigned char qbuf[3][S::kTile];
@@ -425,8 +427,9 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
     const int hi = lane >> 5;
 
     const int logical = xcd_logical_id(blockIdx.x, n_wg);
-    const int bh = __builtin_amdgcn_readfirstlane(logical / n_ktiles);
-    const int kt = __builtin_amdgcn_readfirstlane(logical - bh * n_ktiles);
+    const HeadTile ht = head_tile_of(logical, n_ktiles, CAUSAL ? group : 1);   // causal: tile 0 is the longest
+    const int bh = ht.bh;
+    const int kt = ht.rank;
     const int k0 = kt * C::kRows;
     const size_t head = size_t(bh) * size_t(N) * D;
     const uint32_t head_bytes = uint32_t(N) * C::kRowBytes;
@@ -661,21 +664,25 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
     const auto* K = static_cast<const _Float16*>(k);
     const auto* V = static_cast<const _Float16*>(v);
     const auto* dO = static_cast<const _Float16*>(dout);
+    // Causal grids: tiles of a few heads at a time, longest first (one
+    // workgroup per SIMD-worth of waves: C::kWaves is 4).
+    const int group_q = CAUSAL ? causal_group(n_tiles, n_wg, C::kWavesPerSimdQ) : 1;
+    const int group_kv = CAUSAL ? causal_group(n_tiles, n_wg, C::kWavesPerSimdKV) : 1;
     hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream, Q,
                        K, V, static_cast<const _Float16*>(o), dO, lse, static_cast<_Float16*>(dq),
-                       delta, N, n_tiles, n_wg, c2, sigma);
+                       delta, N, n_tiles, n_wg, group_q, c2, sigma);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (D == 128) {
         hipLaunchKernelGGL((fa2_bwd_dkdv_stream_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0,
                            stream, Q, K, V, dO, lse, static_cast<const float*>(delta),
                            static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
-                           c2, sigma);
+                           group_kv, c2, sigma);
     } else {
         hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                            Q, K, V, dO, lse, static_cast<const float*>(delta),
                            static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
-                           c2, sigma);
+                           group_kv, c2, sigma);
     }
     return hipGetLastError();
 }

@@ -102,5 +102,24 @@ __device__ __forceinline__ int xcd_logical_id(int wg, int n_wg) {
     return (n_wg & 7) == 0 ? (wg & 7) * (n_wg >> 3) + (wg >> 3) : wg;
 }
 
+// (batch*head, tile rank) of a logical id when each head has n_tiles tiles
+// and the tiles are dealt `group` heads at a time, rank-major inside each
+// group (group 1: head by head).  The launch sizes the group (causal_group)
+// so the workgroups an XCD runs together take the same rank of a few heads.
+struct HeadTile {
+    int bh, rank;
+};
+__device__ __forceinline__ HeadTile head_tile_of(int logical, int n_tiles, int group) {
+    if (group > 1) {
+        const int g0 = logical / (group * n_tiles);
+        const int i = logical - g0 * group * n_tiles;
+        const int rank = i / group;
+        return {__builtin_amdgcn_readfirstlane(g0 * group + (i - rank * group)),
+                __builtin_amdgcn_readfirstlane(rank)};
+    }
+    const int bh = __builtin_amdgcn_readfirstlane(logical / n_tiles);
+    return {bh, __builtin_amdgcn_readfirstlane(logical - bh * n_tiles)};
+}
+
 }  // namespace dev
 }  // namespace fa2

@@ -154,21 +154,11 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Logical tile id: consecutive ids (the Q tiles of one head) go to one XCD.
     const int wg = blockIdx.x;
     const int logical = xcd_logical_id(wg, n_wg);
-    int bh, qt;
-    if (CAUSAL && group > 1) {
-        // Longest rows first across `group` heads at a time: consecutive ids
-        // take the same query-tile rank of the group's heads, so the
-        // workgroups an XCD runs together start with the longest tiles of a
-        // few heads (their K/V shared in L2) and the shortest come last.
-        const int g0 = logical / (group * n_qtiles);
-        const int i = logical - g0 * group * n_qtiles;
-        const int rank = i / group;
-        bh = __builtin_amdgcn_readfirstlane(g0 * group + (i - rank * group));
-        qt = __builtin_amdgcn_readfirstlane(rank);
-    } else {
-        bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
-        qt = __builtin_amdgcn_readfirstlane(logical - bh * n_qtiles);
-    }
+    // Causal grids take the query tiles longest first, a few heads at a
+    // time (head_tile_of); the group is 1 otherwise.
+    const HeadTile ht = head_tile_of(logical, n_qtiles, CAUSAL ? group : 1);
+    const int bh = ht.bh;
+    int qt = ht.rank;
     if (CAUSAL) qt = n_qtiles - 1 - qt;   // longest rows first
     const int q0 = qt * C::kBQ;
     const size_t head = size_t(bh) * size_t(N) * D;
@@ -475,17 +465,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     using C = Cfg<D, CAUSAL>;
     const int n_qtiles = (N + C::kBQ - 1) / C::kBQ;
     const int n_wg = n_qtiles * BH;
-    // Causal head groups: about as many heads' query tiles as an XCD (32 CUs)
-    // runs at once, kept whole inside each XCD's range of logical ids;
-    // halved until they fit, 1 = head by head.
-    int group = 1;
-    if (CAUSAL && n_wg % 8 == 0) {
-        const int at_once = 32 * (4 * C::kWavesPerSimd / C::kWaves);   // workgroups per XCD
-        int g = 1;
-        while (2 * g * n_qtiles <= at_once) g *= 2;
-        while (g > 1 && (n_wg / 8) % (g * n_qtiles) != 0) g /= 2;
-        group = g;
-    }
+    const int group = CAUSAL ? causal_group(n_qtiles, n_wg, 4 * C::kWavesPerSimd / C::kWaves) : 1;
     hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                        static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
                        static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, N,

@@ -5,6 +5,19 @@
 
 namespace fa2 {
 
+// Head group for causal grids (head_tile_of): the largest power of two g
+// with g * n_tiles at most the workgroups an XCD (32 of the 256 CUs) runs at
+// once, wgs_per_cu each, and with each XCD's range of n_wg / 8 logical ids a
+// whole number of groups; 1 when none fits.
+inline int causal_group(int n_tiles, int n_wg, int wgs_per_cu) {
+    if (n_wg % 8 != 0 || n_tiles <= 0) return 1;
+    const long at_once = 32L * wgs_per_cu;
+    int g = 1;
+    while (2L * g * n_tiles <= at_once) g *= 2;
+    while (g > 1 && (n_wg / 8) % (g * n_tiles) != 0) g /= 2;
+    return g;
+}
+
 // Launch the forward kernel for already-validated arguments.  Returns the
 // HIP error of the launch (hipSuccess on success).
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o,
