@@ -113,7 +113,7 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
                        const _Float16* __restrict__ V, const _Float16* __restrict__ O,
                        const _Float16* __restrict__ dO, const float* __restrict__ LSE,
                        _Float16* __restrict__ dQ, float* __restrict__ Delta, int N,
-                       int n_qtiles, int n_wg, int group, float c2, float sigma) {
+                       int n_qtiles, int n_wg, float c2, float sigma, int group) {
     using C = BwdCfg<D>;
     // K tile swizzled (plain reads for S^T, transposed reads for dQ^T), V
     // tile chunk-major (plain reads for dP^T).
@@ -244,7 +244,7 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
                          const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
                          const float* __restrict__ LSE, const float* __restrict__ Delta,
                          _Float16* __restrict__ dK, _Float16* __restrict__ dV, int N,
-                         int n_ktiles, int n_wg, int group, float c2, float sigma) {
+                         int n_ktiles, int n_wg, float c2, float sigma, int group) {
     using C = BwdCfg<D>;
     // Q and dO tiles swizzled (plain reads for S and dP, transposed reads for
     // dK^T and dV^T); per-query log2-domain LSE and delta beside them.
@@ -413,7 +413,7 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
                                 const _Float16* __restrict__ V, const _Float16* __restrict__ dO,
                                 const float* __restrict__ LSE, const float* __restrict__ Delta,
                                 _Float16* __restrict__ dK, _Float16* __restrict__ dV, int N,
-                                int n_ktiles, int n_wg, int group, float c2, float sigma) {
+                                int n_ktiles, int n_wg, float c2, float sigma, int group) {
     using C = BwdCfg<D>;
     using S = KvStream<D>;
     __shared__ __attribute__((aligned(16))) unsigned char qbuf[3][S::kTile];
@@ -670,19 +670,19 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
     const int group_kv = CAUSAL ? causal_group(n_tiles, n_wg, C::kWavesPerSimdKV) : 1;
     hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream, Q,
                        K, V, static_cast<const _Float16*>(o), dO, lse, static_cast<_Float16*>(dq),
-                       delta, N, n_tiles, n_wg, group_q, c2, sigma);
+                       delta, N, n_tiles, n_wg, c2, sigma, group_q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (D == 128) {
         hipLaunchKernelGGL((fa2_bwd_dkdv_stream_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0,
                            stream, Q, K, V, dO, lse, static_cast<const float*>(delta),
                            static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
-                           group_kv, c2, sigma);
+                           c2, sigma, group_kv);
     } else {
         hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                            Q, K, V, dO, lse, static_cast<const float*>(delta),
                            static_cast<_Float16*>(dk), static_cast<_Float16*>(dv), N, n_tiles, n_wg,
-                           group_kv, c2, sigma);
+                           c2, sigma, group_kv);
     }
     return hipGetLastError();
 }

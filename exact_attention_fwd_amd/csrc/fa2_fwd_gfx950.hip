@@ -136,8 +136,8 @@ __global__ __launch_bounds__((Cfg<D, CAUSAL>::kThreads))
 __attribute__((amdgpu_waves_per_eu(Cfg<D, CAUSAL>::kWavesPerSimd, Cfg<D, CAUSAL>::kWavesPerSimd)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
-                    float* __restrict__ LSE, int N, int n_qtiles, int n_wg, int group,
-                    float c, uint32_t q_and, uint32_t q_xor) {
+                    float* __restrict__ LSE, int N, int n_qtiles, int n_wg, float c,
+                    uint32_t q_and, uint32_t q_xor, int group) {
     using C = Cfg<D, CAUSAL>;
     static_assert(C::schedule_ok(), "P chunk rewritten before its last reader");
     __shared__ __attribute__((aligned(16))) unsigned char kb0[C::kTileBytes];
@@ -469,7 +469,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                        static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
                        static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, N,
-                       n_qtiles, n_wg, group, c, q_and, q_xor);
+                       n_qtiles, n_wg, c, q_and, q_xor, group);
     return hipGetLastError();
 }
 
