@@ -62,10 +62,10 @@ struct BwdCfg {
     static constexpr int kStage = kChunks / kWaves;    // staged chunks per thread per tensor and tile
     // The dK/dV kernel keeps K^T, V^T and two accumulators of D x 32 per
     // wave: at D = 128 that needs the registers of a whole SIMD.  The dQ
-    // kernel fits three waves per SIMD up to D = 64 (measured 1-4 % faster
-    // than two).
-    static constexpr int kWavesPerSimdQ = D <= 64 ? 3 : 2;
-    static constexpr int kWavesPerSimdKV = D >= 128 ? 1 : 2;
+    // kernel fits four waves per SIMD at D = 32 (1-3 % faster than three) and
+    // three at D = 64 (1-4 % faster than two; four spill there, 6 % slower).
+    static constexpr int kWavesPerSimdQ = D <= 32 ? 4 : D <= 64 ? 3 : 2;
+    static constexpr int kWavesPerSimdKV = D >= 128 ? 1 : D <= 32 ? 3 : 2;   // d = 32: three, 3-4 % faster
 };
 
 __device__ __forceinline__ f32x16 mfma(const h8& a, const h8& b, const f32x16& c) {
