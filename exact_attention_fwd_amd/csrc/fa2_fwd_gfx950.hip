@@ -21,8 +21,9 @@
 //    non-causal d = 64, and 4 waves (128 queries) otherwise: 8 waves halve
 //    the K/V staging per query, while under the causal mask at d = 64 the
 //    smaller group wastes fewer masked keys on the diagonal.  Two waves share
-//    each SIMD, except at d = 256, where a wave's 32x256 fp32 accumulator
-//    needs the registers of a whole SIMD.
+//    each SIMD; three at d = 32, whose registers allow it; one at d = 256,
+//    where a wave's 32x256 fp32 accumulator needs the registers of a whole
+//    SIMD.
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_f16 (A = 32 keys x 16 dims from LDS, B = Q^T held in
 //    registers for the whole loop).  In the 32x32 accumulator a lane then
@@ -95,11 +96,12 @@ constexpr int kAhead = 4;                // LDS operand reads in flight ahead of
 template <int D, bool CAUSAL>
 struct Cfg {
     // Waves per workgroup (see the header): 8 at d = 128 and at non-causal
-    // d = 64, 4 otherwise.  Two waves per SIMD, except at d = 256, whose
-    // registers need a SIMD each.
+    // d = 64, 4 otherwise.  Two waves per SIMD; three at d = 32 (measured
+    // 6-7 % faster non-causal than two); one at d = 256, whose registers need
+    // a SIMD each.
     static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
     static constexpr int kWaves = (D == 128 || (D == 64 && !CAUSAL)) ? 8 : 4;
-    static constexpr int kWavesPerSimd = D == 256 ? 1 : 2;
+    static constexpr int kWavesPerSimd = D == 256 ? 1 : D == 32 ? 3 : 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBQ = kWaves * kQW;               // query rows per workgroup
     static constexpr int kRowBytes = D * 2;
