@@ -25,7 +25,7 @@ Sources (cited by page title and section; the pages are web articles):
   notes; [GPU-MODE-50]): the one-query-block FA2 pseudocode, which returns
   O / l together with m and l.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * the scale used is the float32 value that crosses the C ABI, widened to
   float64 exactly (``sigma = float(np.float32(scale))``);

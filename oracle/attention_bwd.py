@@ -23,7 +23,7 @@ so this module is the chain rule written out:
 Masked entries have P_ij = 0 and so dS_ij = 0.  The row term
 sum_k P_ik dP_ik equals dO_i . O_i; it is returned as ``delta``.
 
-Readings taken where the pages are silent (listed in the design doc): the loss is
+Readings taken where the pages are silent: the loss is
 <dO, O> (dO is the upstream gradient, any values); the scale is the fp32
 value the kernel receives, widened exactly, as in the forward oracle; the
 gradients are returned in float64, not rounded.
