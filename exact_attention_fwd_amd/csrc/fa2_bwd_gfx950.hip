@@ -161,6 +161,13 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
     const float delta = pair_sum(dsum);
     const float lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, my_q * 4, 0, 0)) * kLog2e;
     if (hi == 0 && my_q < N) Delta[size_t(bh) * N + my_q] = delta;
+    // -delta in every element: the dP^T products accumulate onto it, so they
+    // return dP - delta.  (Opaque to the compiler: kept in registers rather
+    // than rebuilt from delta for every block.)
+    f32x16 ndelta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndelta[r] = -delta;
+    asm volatile("" : "+v"(ndelta));
 
     const int kv_end = CAUSAL ? min(N, q0 + C::kRows) : N;
     const int n_kt = (kv_end + kBK - 1) / kBK;
@@ -204,13 +211,13 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
         const bool masked = t >= n_full;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {   // 32 keys at a time
-            f32x16 st = f32x16{}, dpt = f32x16{};
+            f32x16 st = f32x16{}, dpt;   // dpt: dP^T - delta
 #pragma unroll
             for (int ds = 0; ds < C::kDSteps; ++ds) {
                 const h8 ak = *reinterpret_cast<const h8*>(kb + ksw.b[ds & 1] + sw_imm(ds, blk));
                 st = mfma(ak, qf[ds], st);
                 const h8 av = *reinterpret_cast<const h8*>(vb + v_base + lds_k_off(2 * ds, 32 * blk));
-                dpt = mfma(av, dof[ds], dpt);
+                dpt = mfma(av, dof[ds], ds == 0 ? ndelta : dpt);
             }
             // Register r of this lane: key t*64 + 32*blk + 8*(r/4) + 4*hi + r%4.
             h8 dsf[2];
@@ -221,7 +228,7 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
                     const int key = t * kBK + 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
                     if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
                 }
-                dsf[r >> 3][r & 7] = (_Float16)(p * (dpt[r] - delta));
+                dsf[r >> 3][r & 7] = (_Float16)(p * dpt[r]);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
