@@ -317,7 +317,7 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
             *reinterpret_cast<u32x4*>(ob + lds_v_off(ch, lane)) = so[j];
         }
         if (wave == 0) lb[lane] = sl;
-        if (wave == 1) dbuf[lane] = sd;
+        if (wave == 1) dbuf[lane] = -sd;   // -delta: the dP products accumulate onto it
     };
     const SwBase sw(lane);
     const TrBase tr(lane);
@@ -343,29 +343,37 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
         const bool masked = CAUSAL && t < t_mask_end;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {   // 32 queries at a time
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // -delta of the block's queries in the accumulator's register order.
+            f32x16 nd;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 Dl = *reinterpret_cast<const float4*>(dlb + 32 * blk + 8 * g + 4 * hi);
+                nd[4 * g] = Dl.x;
+                nd[4 * g + 1] = Dl.y;
+                nd[4 * g + 2] = Dl.z;
+                nd[4 * g + 3] = Dl.w;
+            }
+            f32x16 s = f32x16{}, dp;   // dp: dP - delta
 #pragma unroll
             for (int ds = 0; ds < C::kDSteps; ++ds) {
                 const h8 aq = *reinterpret_cast<const h8*>(qb + sw.b[ds & 1] + sw_imm(ds, blk));
                 s = mfma(aq, kf[ds], s);
                 const h8 ao = *reinterpret_cast<const h8*>(ob + sw.b[ds & 1] + sw_imm(ds, blk));
-                dp = mfma(ao, vf[ds], dp);
+                dp = mfma(ao, vf[ds], ds == 0 ? nd : dp);
             }
             // Register r = 4g + k of this lane: query t*64 + 32*blk + 8g + 4*hi + k.
             h8 pf[2], dsf[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 L = *reinterpret_cast<const float4*>(lb + 32 * blk + 8 * g + 4 * hi);
-                const float4 Dl = *reinterpret_cast<const float4*>(dlb + 32 * blk + 8 * g + 4 * hi);
                 const float lv[4] = {L.x, L.y, L.z, L.w};
-                const float dv4[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int r = 4 * g + k;
                     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lv[k]));
                     if (masked && my_k > t * kBK + 32 * blk + 8 * g + 4 * hi + k) p = 0.f;
                     pf[r >> 3][r & 7] = (_Float16)p;
-                    dsf[r >> 3][r & 7] = (_Float16)(p * (dp[r] - dv4[k]));
+                    dsf[r >> 3][r & 7] = (_Float16)(p * dp[r]);
                 }
             }
 #pragma unroll
