@@ -491,7 +491,9 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
             *reinterpret_cast<u32x4*>(&obuf[b][0] + lds_v_off(ch, lane)) = so[j];
         }
         if (wave == 0) lbuf[b][lane] = sl;
-        if (wave == 1) dbuf[b][lane] = sd;
+        // Non-causal: -delta, onto which the dP products accumulate (measured
+        // 2.5-5 % faster there; 3 % slower causal, which subtracts delta).
+        if (wave == 1) dbuf[b][lane] = CAUSAL ? sd : -sd;
     };
     const SwBase sw(lane);
     const TrBase tr(lane);
@@ -515,8 +517,22 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
     fetch(t0 + 1);
     put(1);
     __syncthreads();
+    // -delta of the 16 query rows of block b's half of LDS buffer `buf`, in
+    // the accumulator's register order (register 4g + k: row 32*half + 8g + 4*hi + k).
+    auto neg_delta = [&](int buf, int half) {
+        f32x16 nd;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 Dv = *reinterpret_cast<const float4*>(&dbuf[buf][0] + 32 * half + 8 * g + 4 * hi);
+            nd[4 * g] = Dv.x;
+            nd[4 * g + 1] = Dv.y;
+            nd[4 * g + 2] = Dv.z;
+            nd[4 * g + 3] = Dv.w;
+        }
+        return nd;
+    };
     {
-        f32x16 a = f32x16{}, b = f32x16{};
+        f32x16 a = f32x16{}, b = CAUSAL ? f32x16{} : neg_delta(0, 0);   // non-causal b: dP - delta
 #pragma unroll
         for (int ds = 0; ds < C::kDSteps; ++ds) {
             a = mfma(*reinterpret_cast<const h8*>(&qbuf[0][0] + sw.b[ds & 1] + sw_imm(ds, 0)), kf[ds], a);
@@ -539,17 +555,20 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
         const unsigned char* qb_next = &qbuf[((j + 1) >> 1) % 3][0];
         const unsigned char* ob_next = &obuf[((j + 1) >> 1) % 3][0];
         const float* lb = &lbuf[ti % 3][0];
-        const float* dlb = &dbuf[ti % 3][0];
         constexpr int PREV = 1 - PAR;                  // parity of blocks j-1 and j+1
+        // Non-causal: the dP products of block j+1 accumulate onto -delta of its rows.
+        const f32x16 nd_next = CAUSAL ? f32x16{} : neg_delta(((j + 1) >> 1) % 3, PREV);
         // Row statistics of block j's 16 query rows of this lane (register r =
         // 4g + k: row 32*PAR + 8g + 4*hi + k of the tile).
-        float Lr[16], Dr[16];
+        float Lr[16], Dr[16];   // Dr: delta (causal only)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const float4 L = *reinterpret_cast<const float4*>(lb + 32 * PAR + 8 * g + 4 * hi);
-            const float4 Dv = *reinterpret_cast<const float4*>(dlb + 32 * PAR + 8 * g + 4 * hi);
             Lr[4 * g] = L.x; Lr[4 * g + 1] = L.y; Lr[4 * g + 2] = L.z; Lr[4 * g + 3] = L.w;
-            Dr[4 * g] = Dv.x; Dr[4 * g + 1] = Dv.y; Dr[4 * g + 2] = Dv.z; Dr[4 * g + 3] = Dv.w;
+            if (CAUSAL) {
+                const float4 Dv = *reinterpret_cast<const float4*>(&dbuf[ti % 3][0] + 32 * PAR + 8 * g + 4 * hi);
+                Dr[4 * g] = Dv.x; Dr[4 * g + 1] = Dv.y; Dr[4 * g + 2] = Dv.z; Dr[4 * g + 3] = Dv.w;
+            }
         }
         const int q0 = (t0 + ti) * kBK + 32 * PAR;     // first query of block j
         const bool masked = CAUSAL && q0 < kw0 + kQW - 1;
@@ -577,7 +596,7 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
                 else dv[db] = mfma(a, pf[PREV][kk], dv[db]);
             } else {
                 const int q = p - S::kPV, ds = q >> 1, which = q & 1;
-                if (which) dp_[PREV] = mfma(a, vf[ds], ds == 0 ? f32x16{} : dp_[PREV]);
+                if (which) dp_[PREV] = mfma(a, vf[ds], ds == 0 ? nd_next : dp_[PREV]);
                 else s_[PREV] = mfma(a, kf[ds], ds == 0 ? f32x16{} : s_[PREV]);
             }
         };
@@ -594,7 +613,7 @@ void fa2_bwd_dkdv_stream_kernel(const _Float16* __restrict__ Q, const _Float16* 
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int r = 2 * q + h;
-                    const float d_ = pe[r] * (dp_[PAR][r] - Dr[r]);
+                    const float d_ = CAUSAL ? pe[r] * (dp_[PAR][r] - Dr[r]) : pe[r] * dp_[PAR][r];
                     pf[PAR][r >> 3][r & 7] = (_Float16)pe[r];
                     dsf[PAR][r >> 3][r & 7] = (_Float16)d_;
                 }
