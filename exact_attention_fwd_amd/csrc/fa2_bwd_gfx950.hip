@@ -220,16 +220,23 @@ void fa2_bwd_dq_kernel(const _Float16* __restrict__ Q, const _Float16* __restric
                 dpt = mfma(av, dof[ds], ds == 0 ? ndelta : dpt);
             }
             // Register r of this lane: key t*64 + 32*blk + 8*(r/4) + 4*hi + r%4.
+            // Exponent arguments; hidden keys (past N, or after the query
+            // under the causal mask) get -inf, i.e. P = 0, in a branch of
+            // their own that only the tiles crossing N or the diagonal take.
+            float arg[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) arg[r] = __builtin_fmaf(st[r], c2, -lse2);
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t * kBK + 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (key >= N || (CAUSAL && key > my_q)) arg[r] = -INFINITY;
+                }
+            }
             h8 dsf[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c2, -lse2));
-                if (masked) {
-                    const int key = t * kBK + 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
-                }
-                dsf[r >> 3][r & 7] = (_Float16)(p * dpt[r]);
-            }
+            for (int r = 0; r < 16; ++r)
+                dsf[r >> 3][r & 7] = (_Float16)(__builtin_amdgcn_exp2f(arg[r]) * dpt[r]);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -362,19 +369,28 @@ void fa2_bwd_dkdv_kernel(const _Float16* __restrict__ Q, const _Float16* __restr
                 dp = mfma(ao, vf[ds], ds == 0 ? nd : dp);
             }
             // Register r = 4g + k of this lane: query t*64 + 32*blk + 8g + 4*hi + k.
-            h8 pf[2], dsf[2];
+            // Exponent arguments; under the causal mask the queries before
+            // this key get -inf (P = 0) in a branch of its own that only the
+            // tiles crossing the diagonal take.
+            float arg[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 L = *reinterpret_cast<const float4*>(lb + 32 * blk + 8 * g + 4 * hi);
                 const float lv[4] = {L.x, L.y, L.z, L.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int r = 4 * g + k;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lv[k]));
-                    if (masked && my_k > t * kBK + 32 * blk + 8 * g + 4 * hi + k) p = 0.f;
-                    pf[r >> 3][r & 7] = (_Float16)p;
-                    dsf[r >> 3][r & 7] = (_Float16)(p * dp[r]);
-                }
+                for (int k = 0; k < 4; ++k) arg[4 * g + k] = __builtin_fmaf(s[4 * g + k], c2, -lv[k]);
+            }
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (my_k > t * kBK + 32 * blk + 8 * (r >> 2) + 4 * hi + (r & 3)) arg[r] = -INFINITY;
+            }
+            h8 pf[2], dsf[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(arg[r]);
+                pf[r >> 3][r & 7] = (_Float16)p;
+                dsf[r >> 3][r & 7] = (_Float16)(p * dp[r]);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
