@@ -7,7 +7,8 @@ Gates (tests/parity.py): per tensor, the error in units of its rounding
 bound u (|G| + E + 2^-14) -- E the oracle's per-element error scale -- is at
 most 2 everywhere and 0.5 in rms.  Cases: odd N at every supported head dim, causal
 and not; batch x heads with a ragged tail; the reference shape
-[4,32,2048,64] and [4,16,2048,128] (every element); stress inputs that move
+[4,32,2048,64] and [4,16,2048,128] (every element); long sequences, N = 8192
+(every element of two heads); stress inputs that move
 the row max or concentrate the weights; scale 0 / negative / small; closed
 forms (Q = 0: dK = 0 exactly; N = 1: dV = dO exactly, dQ and dK ~ 0);
 determinism and guard bands; d = 256 rejected.
@@ -68,6 +69,15 @@ def test_batch_heads_and_ragged_tail_together(d):
 def test_full_size(shape, causal):
     q, k, v = make_qkv(*shape, 1.0, seed=0)
     check_bwd(f"{list(shape)} causal={causal}", q, k, v, _do(shape, 0), shape[3] ** -0.5, causal)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (128, False), (128, True)])
+def test_long_sequence(d, causal):
+    """N = 8192: 128 tiles of 64 rows per head, so each kernel's loop runs 128
+    (causal: up to 128) tiles and the causal grid deals one head at a time."""
+    shape = (1, 2, 8192, d)
+    q, k, v = make_qkv(*shape, 1.0, seed=5)
+    check_bwd(f"{list(shape)} causal={causal}", q, k, v, _do(shape, 5), d ** -0.5, causal)
 
 
 @pytest.mark.parametrize("kind", ["rising", "falling", "large", "const_v", "zero_q"])
