@@ -25,10 +25,15 @@
 //    dK^T += Q^T dS with Q^T and dO^T read transposed from LDS.
 //  In both, an accumulator's register order is the B operand of the next
 //  product (fa2_device.h), so P and dS never leave registers.
+//  The dP products start their accumulation from -delta of their query rows
+//  (except in the causal d = 128 kernel), so they return dP - delta and dS
+//  is one multiply.
 //  Tiles of 64 rows are double-buffered in LDS through registers (the next
 //  tile's loads are issued before the current tile's products), one barrier
-//  per tile.  Causal work stops at the diagonal; the tiles that cross it are
-//  masked.  Rows past N read as zero through the per-head buffer resources,
+//  per tile.  Causal work stops at the diagonal; the tiles that cross it (and
+//  the key tile that crosses N) are masked in a branch of their own, which
+//  sets the exponent argument to -inf; causal grids take the longest tiles
+//  first, a few heads at a time.  Rows past N read as zero through the per-head buffer resources,
 //  which makes their contributions exactly zero, and their stores are
 //  dropped.
 
