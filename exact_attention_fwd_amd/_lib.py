@@ -18,9 +18,11 @@ FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_MISALIGNED = 3
 FA2_ERR_NO_DEVICE = 4
 FA2_ERR_LAUNCH = 5
+FA2_ERR_SCRATCH_LIMIT = 6
+FA2_NOALLOC_SCRATCH_BYTES = 8 << 20   # the fixed scratch of fa2_fwd_splitkv_noalloc
 
 EXPORTED = ("fa2_fwd", "fa2_bwd", "fa1_fwd", "fa1_workspace_bytes", "fa2_fwd_splitkv",
-            "fa2_splitkv_splits", "fa2_splitkv_workspace_bytes", "fa2_lse_merge",
+            "fa2_fwd_splitkv_noalloc", "fa2_splitkv_splits", "fa2_splitkv_workspace_bytes", "fa2_lse_merge",
             "fa2_status_string", "fa2_last_hip_error", "fa2_version")
 
 _lock = threading.Lock()
@@ -60,6 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_fwd_splitkv.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_size_t] + [
             ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.fa2_fwd_splitkv.restype = ctypes.c_int
+        lib.fa2_fwd_splitkv_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa2_fwd_splitkv_noalloc.restype = ctypes.c_int
         lib.fa2_splitkv_splits.argtypes = [ctypes.c_int] * 6
         lib.fa2_splitkv_splits.restype = ctypes.c_int
         lib.fa2_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 6
@@ -105,6 +110,14 @@ def fa2_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d, scale, n_spl
     return load_library().fa2_fwd_splitkv(q, k, v, o, lse, ws, int(ws_bytes), int(B), int(H),
                                           int(Nq), int(Nk), int(d), float(scale), int(n_splits),
                                           stream)
+
+
+def fa2_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, n_splits, stream) -> int:
+    """The C entry point of the split key/value forward that allocates
+    nothing (the library's fixed scratch holds the partial results)."""
+    return load_library().fa2_fwd_splitkv_noalloc(q, k, v, o, lse, int(B), int(H), int(Nq),
+                                                  int(Nk), int(d), float(scale), int(n_splits),
+                                                  stream)
 
 
 def fa2_splitkv_splits(B, H, Nq, Nk, d, n_splits=0) -> int:
@@ -276,6 +289,36 @@ def fwd_splitkv(q, k, v, scale=None, n_splits=0, out=None, lse=None, workspace=N
                              stream)
     if status != FA2_OK:
         raise Fa2Error(status, f"fa2_fwd_splitkv failed: {fa2_status_string(status)} "
+                               f"(hip error {fa2_last_hip_error()})")
+    return out, lse
+
+
+def fwd_splitkv_noalloc(q, k, v, out, lse, scale=None, n_splits=0, stream=None):
+    """``fwd_splitkv`` through the entry point that allocates nothing: the
+    caller passes the outputs (``out`` fp16 [B, H, Nq, d], ``lse`` fp32
+    [B, H, Nq]) and the partial results go to the library's fixed scratch
+    buffer (FA2_NOALLOC_SCRATCH_BYTES per GPU).  Calls on one GPU must not
+    overlap in time.  Returns (out, lse)."""
+    import torch
+
+    _check_qkv((("k", k), ("v", v)))
+    _check_qkv((("q", q),))
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[:2] != q.shape[:2] or k.shape[3] != d or k.device != q.device:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d], on one device")
+    if out is None or lse is None:
+        raise ValueError("out and lse must be passed: this entry point allocates nothing")
+    if scale is None:
+        scale = d ** -0.5
+    out = _out(out, q, torch.float16, q.shape, "out")
+    lse = _out(lse, q, torch.float32, (B, H, Nq), "lse")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = fa2_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, Nq, Nk, d, scale, n_splits, stream)
+    if status != FA2_OK:
+        raise Fa2Error(status, f"fa2_fwd_splitkv_noalloc failed: {fa2_status_string(status)} "
                                f"(hip error {fa2_last_hip_error()})")
     return out, lse
 

@@ -170,35 +170,79 @@ extern "C" size_t fa2_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int 
     return splitkv_ws_bytes(B, H, Nq, d, fa2::plan_splits(B * H, Nq, Nk, n_splits));
 }
 
-extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                               void* ws, size_t ws_bytes, int B, int H, int Nq, int Nk, int d,
-                               float scale, int n_splits, void* stream) {
+namespace {
+
+// The checks of a split key/value call that do not involve its workspace,
+// all before any HIP call; on success fills the plan and the workspace bytes
+// it needs.
+int check_splitkv_call(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                       int n_splits, fa2::SplitPlan* plan, size_t* w_bytes) {
     if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
     if (const int st = check_splitkv_sizes(B, H, Nq, Nk, d, scale, n_splits)) return st;
-    const fa2::SplitPlan plan = fa2::plan_splits(B * H, Nq, Nk, n_splits);
+    *plan = fa2::plan_splits(B * H, Nq, Nk, n_splits);
     // one workgroup per (32-query tile, key range, batch * head)
-    if (int64_t(B) * H * ((Nq + 31) / 32) * plan.n_splits > INT32_MAX) return FA2_ERR_INVALID_ARG;
-    const size_t w_bytes = splitkv_ws_bytes(B, H, Nq, d, plan);
-    if (w_bytes && (!ws || ws_bytes < w_bytes)) return FA2_ERR_INVALID_ARG;
-    uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-                     reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
-                     reinterpret_cast<uintptr_t>(lse);
-    if (w_bytes) bits |= reinterpret_cast<uintptr_t>(ws);
+    if (int64_t(B) * H * ((Nq + 31) / 32) * plan->n_splits > INT32_MAX) return FA2_ERR_INVALID_ARG;
+    *w_bytes = splitkv_ws_bytes(B, H, Nq, d, *plan);
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(lse);
     if (bits & 15u) return FA2_ERR_MISALIGNED;
     const size_t q_bytes = size_t(B) * H * Nq * size_t(d) * 2;
     const size_t kv_bytes = size_t(B) * H * Nk * size_t(d) * 2;
     const size_t l_bytes = size_t(B) * H * Nq * 4;
     const struct { const void* p; size_t n; } ins[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}};
-    const struct { const void* p; size_t n; } outs[] = {{o, q_bytes}, {lse, l_bytes}, {ws, w_bytes}};
-    for (const auto& w : outs) {
-        if (!w.n) continue;
-        for (const auto& r : ins)
-            if (overlaps(w.p, w.n, r.p, r.n)) return FA2_ERR_INVALID_ARG;
-        for (const auto& w2 : outs)
-            if (&w2 != &w && w2.n && overlaps(w.p, w.n, w2.p, w2.n)) return FA2_ERR_INVALID_ARG;
+    for (const auto& r : ins) {
+        if (overlaps(o, q_bytes, r.p, r.n) || overlaps(lse, l_bytes, r.p, r.n))
+            return FA2_ERR_INVALID_ARG;
+    }
+    if (overlaps(o, q_bytes, lse, l_bytes)) return FA2_ERR_INVALID_ARG;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               void* ws, size_t ws_bytes, int B, int H, int Nq, int Nk, int d,
+                               float scale, int n_splits, void* stream) {
+    fa2::SplitPlan plan;
+    size_t w_bytes = 0;
+    if (const int st = check_splitkv_call(q, k, v, o, lse, B, H, Nq, Nk, d, scale, n_splits, &plan,
+                                          &w_bytes))
+        return st;
+    if (w_bytes) {
+        if (!ws || ws_bytes < w_bytes) return FA2_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(ws) & 15u) return FA2_ERR_MISALIGNED;
+        const size_t q_bytes = size_t(B) * H * Nq * size_t(d) * 2;
+        const size_t kv_bytes = size_t(B) * H * Nk * size_t(d) * 2;
+        const size_t l_bytes = size_t(B) * H * Nq * 4;
+        const struct { const void* p; size_t n; } others[] = {
+            {q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}, {o, q_bytes}, {lse, l_bytes}};
+        for (const auto& r : others)
+            if (overlaps(ws, w_bytes, r.p, r.n)) return FA2_ERR_INVALID_ARG;
     }
     return launch_status(fa2::launch_splitkv(q, k, v, o, lse, w_bytes ? ws : nullptr, B * H, Nq, Nk,
                                              d, scale, plan, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int fa2_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                                       int n_splits, void* stream) {
+    fa2::SplitPlan plan;
+    size_t w_bytes = 0;
+    if (const int st = check_splitkv_call(q, k, v, o, lse, B, H, Nq, Nk, d, scale, n_splits, &plan,
+                                          &w_bytes))
+        return st;
+    if (w_bytes > FA2_NOALLOC_SCRATCH_BYTES) return FA2_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (w_bytes) {
+        // The library's own buffer (no allocation); its per-device address
+        // is looked up on the first call on a device.
+        const hipError_t e = fa2::noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+        if (e != hipSuccess) return launch_status(e);
+    }
+    return launch_status(fa2::launch_splitkv(q, k, v, o, lse, ws, B * H, Nq, Nk, d, scale, plan,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int fa2_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
@@ -234,6 +278,9 @@ extern "C" const char* fa2_status_string(int status) {
         case FA2_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case FA2_ERR_NO_DEVICE: return "no usable gfx950 device";
         case FA2_ERR_LAUNCH: return "kernel launch failed";
+        case FA2_ERR_SCRATCH_LIMIT:
+            return "the call needs more scratch than fa2_fwd_splitkv_noalloc's fixed buffer "
+                   "(FA2_NOALLOC_SCRATCH_BYTES) holds: use fewer key ranges or fa2_fwd_splitkv";
         default: return "unknown status";
     }
 }

@@ -50,6 +50,11 @@ SplitPlan plan_splits(int BH, int Nq, int Nk, int requested);
 hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                           void* ws, int BH, int Nq, int Nk, int d, float scale,
                           const SplitPlan& plan, hipStream_t stream);
+// The calling device's copy of the library's fixed scratch buffer
+// (FA2_NOALLOC_SCRATCH_BYTES; the device of `stream`, or the current one for
+// the null stream).  The address is looked up with hipGetSymbolAddress on
+// the first call for a device and kept; nothing is allocated.
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
 // Merge of n_parts partial results [n_parts, rows, d] fp32 with their LSE.
 hipError_t launch_lse_merge(const float* opart, const float* lpart, void* o, float* lse,
                             int n_parts, int rows, int d, hipStream_t stream);

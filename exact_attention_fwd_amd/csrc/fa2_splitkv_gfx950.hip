@@ -28,8 +28,10 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
+#include "fa2.h"
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -303,6 +305,43 @@ hipError_t launch_splitkv_t(const void* q, const void* k, const void* v, void* o
 }
 
 }  // namespace
+
+// Fixed scratch of fa2_fwd_splitkv_noalloc: the partial outputs and
+// log-sum-exps of the key ranges, for callers that cannot allocate.  Every
+// device that runs the library holds its own copy until the process ends.
+// Host code never takes the array's name as a device address (on the host
+// it names a stand-in): the address comes from hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[FA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream != nullptr && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // Once per device, with that device current.  Two threads racing
+        // here look up the same address.
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 SplitPlan plan_splits(int BH, int Nq, int Nk, int requested) {
     const int n_tk = (Nk + kBK - 1) / kBK;

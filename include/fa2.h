@@ -20,7 +20,9 @@
  *
  * All functions are plain C, thread-safe and re-entrant; the library keeps no
  * state between calls and allocates no device memory (the backward pass
- * takes its one workspace, delta, from the caller).
+ * takes its one workspace, delta, from the caller) -- except the fixed
+ * scratch buffer of fa2_fwd_splitkv_noalloc, one per GPU, whose calls on one
+ * GPU must not overlap.
  */
 #ifndef FA2_H_
 #define FA2_H_
@@ -40,7 +42,9 @@ typedef enum {
                                 (fa2_bwd: 32, 64, 96, 128)                     */
     FA2_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned                  */
     FA2_ERR_NO_DEVICE = 4,   /* no usable gfx950 device / HIP runtime failure  */
-    FA2_ERR_LAUNCH = 5       /* the kernel launch failed                       */
+    FA2_ERR_LAUNCH = 5,      /* the kernel launch failed                       */
+    FA2_ERR_SCRATCH_LIMIT = 6 /* fa2_fwd_splitkv_noalloc: the call needs more
+                                scratch than FA2_NOALLOC_SCRATCH_BYTES         */
 } fa2_status;
 
 /*
@@ -180,6 +184,34 @@ int fa2_splitkv_splits(int B, int H, int Nq, int Nk, int d, int n_splits);
 /* Workspace bytes fa2_fwd_splitkv needs: splits * B * H * Nq * (d + 1) * 4
  * when it uses more than one range, else 0 (also 0 for invalid sizes). */
 size_t fa2_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int n_splits);
+
+/* Bytes of the fixed device scratch of fa2_fwd_splitkv_noalloc (8 MiB). */
+#define FA2_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * fa2_fwd_splitkv_noalloc -- fa2_fwd_splitkv without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments, kernels and results as fa2_fwd_splitkv (bit
+ * for bit, for the same sizes and n_splits), except that the partial outputs
+ * and log-sum-exps of the key ranges go to a fixed scratch buffer inside the
+ * library: FA2_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from the
+ * library's first call on that GPU until the process ends.  The call itself
+ * allocates and frees nothing (no hipMalloc, hipFree or allocating library
+ * routine); the first call on a device looks the buffer's address up once.
+ *
+ * Errors as for fa2_fwd_splitkv; a call whose fa2_splitkv_workspace_bytes
+ * exceeds FA2_NOALLOC_SCRATCH_BYTES returns FA2_ERR_SCRATCH_LIMIT before any
+ * HIP call.  Every call on one GPU shares that GPU's buffer, which keeps the
+ * last call's contents: calls that overlap in time on one GPU (several
+ * streams, or several host threads) race on it and must be serialised by the
+ * caller.  Nothing in the buffer needs to start at zero: each call writes
+ * every element it reads.
+ */
+int fa2_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int n_splits,
+                            void* stream);
 
 /*
  * fa2_lse_merge -- merge n_parts partial attention results over disjoint key

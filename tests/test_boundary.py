@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert fa2.fa2_version().startswith("fa2-gfx950")
     seen = set()
-    for st in range(6):
+    for st in range(7):
         s = fa2.fa2_status_string(st)
         assert s and s not in seen
         seen.add(s)
@@ -265,3 +265,43 @@ def test_lse_merge_rejects(lib, kw, status):
 
 def test_fa1_workspace_size_rejects_huge_grids():
     assert fa2.fa1_workspace_bytes(1 << 16, 1 << 16, 1, 64) == 0
+
+
+# --------------------------------------------------- fa2_fwd_splitkv_noalloc
+def ncall(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=3, Nk=1000, d=64, scale=0.125, n_splits=4):
+    return fa2.fa2_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, n_splits, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), "FA2_ERR_INVALID_ARG"), (dict(lse=0), "FA2_ERR_INVALID_ARG"),
+    (dict(Nq=0), "FA2_ERR_INVALID_ARG"), (dict(Nk=(1 << 22) + 1), "FA2_ERR_INVALID_ARG"),
+    (dict(d=256), "FA2_ERR_UNSUPPORTED"), (dict(n_splits=-1), "FA2_ERR_INVALID_ARG"),
+    (dict(n_splits=5000), "FA2_ERR_INVALID_ARG"), (dict(scale=math.nan), "FA2_ERR_INVALID_ARG"),
+    (dict(k=K + 8), "FA2_ERR_MISALIGNED"), (dict(o=Q + 16), "FA2_ERR_INVALID_ARG"),
+    (dict(lse=O + 16), "FA2_ERR_INVALID_ARG"), (dict(o=V), "FA2_ERR_INVALID_ARG")])
+def test_noalloc_rejects(lib, kw, status):
+    assert ncall(**kw) == getattr(fa2, status)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    # 4096 ranges x 64 heads x 129 floats of partial results: 135 MB, more
+    # than the fixed 8 MiB; the same call with a workspace is valid
+    a = dict(B=1, H=64, Nq=1, Nk=4096 * 64, d=128, n_splits=4096)
+    need = fa2.fa2_splitkv_workspace_bytes(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], 4096)
+    assert need == 4096 * 64 * 129 * 4 > fa2.FA2_NOALLOC_SCRATCH_BYTES
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40)   # 4.3 GB K and V
+    assert ncall(**far, **a) == fa2.FA2_ERR_SCRATCH_LIMIT
+    assert "fixed buffer" in fa2.fa2_status_string(fa2.FA2_ERR_SCRATCH_LIMIT)
+    # the argument checks come first
+    assert ncall(**dict(far, o=(2 << 40) + 64), **a) == fa2.FA2_ERR_INVALID_ARG
+    assert ncall(**far, **dict(a, d=48)) == fa2.FA2_ERR_UNSUPPORTED
+
+
+def test_noalloc_scratch_covers_the_decode_workloads():
+    # every decoding workload, with the library's split count, fits the
+    # fixed scratch (so the no-allocation entry point serves them)
+    from exact_attention_fwd_amd.workloads import WORKLOADS
+    for w in WORKLOADS.values():
+        if w.Nq:
+            assert fa2.fa2_splitkv_workspace_bytes(w.B, w.H, w.nq, w.N, w.d, 0) <= \
+                fa2.FA2_NOALLOC_SCRATCH_BYTES, w.name
