@@ -556,21 +556,27 @@ def main():
     if args.impl == "fa1":
         result["config"]["impl"] = "FA1 loop order (fa1_fwd)"
     if not args.no_parity and args.which == "bwd":
-        # the first two heads of the timed output, every element, in units of
-        # each gradient's rounding-error bound u (|G| + E + 2^-14)
+        # the first two heads of the timed output, every element: max error in
+        # units of each gradient's worst-case rounding bound u (|G| + E + 2^-14)
+        # (<= 2), rms error in units of the statistical one (u / sqrt 3) S (<= 1)
         from oracle import attention_bwd_fp64
-        from oracle.attention_bwd import attention_bwd_error_scale
+        from oracle.attention_bwd import attention_bwd_error_scale, attention_bwd_error_std
         nh = min(2, w.B * w.H)
         sl = [x.reshape(1, w.B * w.H, w.N, w.d)[:, :nh] for x in (q, k, v, do)]
         ref = attention_bwd_fp64(*sl, w.scale, causal=w.causal)
         esc = attention_bwd_error_scale(*sl, w.scale, causal=w.causal)
+        sdv = attention_bwd_error_std(*sl, w.scale, causal=w.causal)
         got = [t.reshape(1, w.B * w.H, *t.shape[2:])[:, :nh].cpu().numpy().astype(np.float64)
                for t in (gq, gk, gv, gdelta)]
         u = 2.0 ** -11
-        ratios = {name: float((np.abs(g - r) / (u * (np.abs(r) + e + 2.0 ** -14))).max())
-                  for name, g, r, e in zip(("dq", "dk", "dv", "delta"), got, ref, esc)}
+        ratios, rms = {}, {}
+        for name, g, r, e, sd in zip(("dq", "dk", "dv", "delta"), got, ref, esc, sdv):
+            ratios[name] = float((np.abs(g - r) / (u * (np.abs(r) + e + 2.0 ** -14))).max())
+            den = float(np.sqrt(np.mean(np.square(sd)))) * u / math.sqrt(3.0)
+            rms[name] = float(np.sqrt(np.mean(np.square(g - r)))) / den if den > 0 else 0.0
         result["parity"] = {"heads": nh, "max_ratio_to_rounding_bound": ratios,
-                            "pass": bool(max(ratios.values()) <= 2.0)}
+                            "rms_ratio_to_statistical_bound": rms,
+                            "pass": bool(max(ratios.values()) <= 2.0 and max(rms.values()) <= 1.0)}
         log(f"[bench] parity {result['parity']}")
     elif not args.no_parity:
         # sampled parity of the timed output, 64 seeded rows per (b, h)

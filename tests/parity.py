@@ -11,17 +11,23 @@ absolute error of ~1e-6 into a spurious relative failure.
 
 Gates of the backward pass (fp16 dQ, dK, dV and fp32 delta against the
 float64 gradient oracle).  No tolerance for gradients is given, so it comes
-from the arithmetic: the forward-error bound of a dot product whose factors
-were rounded to fp16, |fl(sum a b) - sum a b| <~ u sum |a| |b| with
-u = 2^-11.  ``oracle.attention_bwd_error_scale`` gives that scale E per
-element (P and dS rounded to fp16, delta taken from the fp16 O, fp16
-subnormals); with the fp16 rounding of the result itself the bound reads
-u (|G| + E + 2^-14).  Per tensor G:
-  max  |G_gpu - G_ref| / (u (|G_ref| + E + 2^-14))  <= 2
-  rms  (G_gpu - G_ref) / rms(u (|G_ref| + E + 2^-14)) <= 0.5
-An exact emulation of the kernels' roundings stays within 0.9 and 0.23 of
-these on random, stress, causal and scale cases (tests/test_bwd_tolerance.py,
-which also shows that a dropped or misplaced term exceeds them by far).
+from the arithmetic, the rounding of each value the computation keeps in
+fp16 (u = 2^-11), in two forms:
+  max  |G_gpu - G_ref| / (u (|G_ref| + E + 2^-14))      <= 2
+       E from ``oracle.attention_bwd_error_scale``: the worst-case bound
+       u sum |a| |b| of a dot product whose factors were rounded;
+  rms  (G_gpu - G_ref) / rms((u / sqrt 3) S)           <= 1
+       S from ``oracle.attention_bwd_error_std``: the same products added
+       in quadrature, the standard deviation of the error when each
+       rounding is an independent relative error of variance <= u^2 / 3.
+The rms gate is what rejects arithmetic carried out at lower precision or
+biased: an exact emulation of the kernels' fp16 roundings reads 0.6-0.86
+of it, P and dS rounded to bf16 2.7-4.5, round-toward-zero conversions
+1.7-2.2, a uniform 2^-10 scale error 2.3-2.8 (tests/test_bwd_tolerance.py).
+When the backward is handed an O, delta must also meet its definition
+delta_i = sum_c dO_ic O_ic for that O within the fp32 bound of a d-term sum
+of exact products:
+  max |delta_gpu - sum_c dO_ic O_ic| / (d 2^-24 sum_c |dO_ic O_ic|) <= 1.
 """
 from __future__ import annotations
 
@@ -36,7 +42,8 @@ MAX_REL_LSE = 1e-4
 U16 = 2.0 ** -11          # unit roundoff of fp16
 SUB16 = 2.0 ** -14        # fp16 subnormal rounding (2^-25) in units of U16
 MAX_RATIO_GRAD = 2.0
-RMS_RATIO_GRAD = 0.5
+RMS_STAT_GRAD = 1.0
+U32 = 2.0 ** -24          # unit roundoff of fp32
 
 
 @dataclass
@@ -66,38 +73,57 @@ def diff(o_gpu, lse_gpu, o_ref, lse_ref) -> Diff:
 @dataclass
 class GradDiff:
     max_ratio: float   # max |dG| / (u (|G| + E + 2^-14))
-    rms_ratio: float   # rms(dG) / rms(u (|G| + E + 2^-14))
+    rms_stat: float    # rms(dG) / rms((u / sqrt 3) S)
     rms_rel: float     # rms(dG) / rms(G), for information
 
     def ok(self) -> bool:
-        return self.max_ratio <= MAX_RATIO_GRAD and self.rms_ratio <= RMS_RATIO_GRAD
+        return self.max_ratio <= MAX_RATIO_GRAD and self.rms_stat <= RMS_STAT_GRAD
 
     def __str__(self):
-        return (f"max ratio={self.max_ratio:.3f} rms ratio={self.rms_ratio:.3f} "
+        return (f"max ratio={self.max_ratio:.3f} rms stat={self.rms_stat:.3f} "
                 f"(rms rel={self.rms_rel:.2e})")
 
 
-def grad_diff(g_gpu, g_ref, e_scale) -> GradDiff:
-    """Gradient error in units of its rounding-error bound (see above)."""
-    err = np.abs(np.asarray(g_gpu, dtype=np.float64) - g_ref)
-    den = U16 * (np.abs(g_ref) + e_scale + SUB16)
+def grad_diff(g_gpu, g_ref, e_scale, s_std) -> GradDiff:
+    """Gradient error in units of its rounding-error bounds (see above)."""
+    err = np.asarray(g_gpu, dtype=np.float64) - g_ref
     if err.size == 0:
         return GradDiff(0.0, 0.0, 0.0)
-    rms_ref = float(np.sqrt(np.mean(np.square(g_ref))))
+    den = U16 * (np.abs(g_ref) + e_scale + SUB16)
     rms_err = float(np.sqrt(np.mean(np.square(err))))
-    return GradDiff(float((err / den).max()), rms_err / float(np.sqrt(np.mean(np.square(den)))),
+    rms_std = float(np.sqrt(np.mean(np.square(s_std)))) * U16 / np.sqrt(3.0)
+    rms_stat = rms_err / rms_std if rms_std > 0 else (0.0 if rms_err == 0 else np.inf)
+    rms_ref = float(np.sqrt(np.mean(np.square(g_ref))))
+    return GradDiff(float((np.abs(err) / den).max()), rms_stat,
                     rms_err / rms_ref if rms_ref > 0 else rms_err)
 
 
-def run_gpu_bwd(q, k, v, do, scale, causal):
-    """Forward then backward on the GPU; inputs fp16 numpy arrays.  Returns
-    (dq, dk, dv fp16, delta fp32) numpy arrays."""
+def delta_contract(delta_gpu, do, o) -> float:
+    """max |delta - sum_c dO_c O_c| over rows, in units of the fp32 bound of
+    that d-term sum of exact fp16 products (d 2^-24 sum_c |dO_c O_c|), for
+    the O the backward was handed.  <= 1 passes."""
+    prod = np.asarray(do, dtype=np.float64) * np.asarray(o, dtype=np.float64)
+    ref = prod.sum(axis=-1)
+    bound = prod.shape[-1] * U32 * np.abs(prod).sum(axis=-1)
+    err = np.abs(np.asarray(delta_gpu, dtype=np.float64) - ref)
+    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    return float(ratio.max()) if ratio.size else 0.0
+
+
+def run_gpu_bwd(q, k, v, do, scale, causal, o=None, lse=None):
+    """Backward on the GPU; inputs fp16 numpy arrays.  O and LSE come from the
+    GPU forward, unless given (fp16 / fp32 numpy arrays, e.g. the oracle's
+    rounded).  Returns (dq, dk, dv fp16, delta fp32) numpy arrays."""
     import torch
     import exact_attention_fwd_amd as fa2
 
     tq, tk, tv, tdo = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q, k, v, do))
-    o, l = fa2.fwd(tq, tk, tv, scale=scale, causal=causal)
-    dq, dk, dv, delta = fa2.bwd(tq, tk, tv, o, l, tdo, scale=scale, causal=causal)
+    if o is None:
+        to, tl = fa2.fwd(tq, tk, tv, scale=scale, causal=causal)
+    else:
+        to = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float16)).cuda()
+        tl = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).cuda()
+    dq, dk, dv, delta = fa2.bwd(tq, tk, tv, to, tl, tdo, scale=scale, causal=causal)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy(), delta.cpu().numpy()
 

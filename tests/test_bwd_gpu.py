@@ -3,9 +3,12 @@ float64 gradient oracle, on the same seeded inputs, through the C ABI.
 
 The GPU forward supplies O and LSE (as a caller would); the oracle works
 from Q, K, V and dO alone, so the gates cover the forward's rounding too.
-Gates (tests/parity.py): per tensor, the error in units of its rounding
-bound u (|G| + E + 2^-14) -- E the oracle's per-element error scale -- is at
-most 2 everywhere and 0.5 in rms.  Cases: odd N at every supported head dim, causal
+Gates (tests/parity.py): per tensor, the error in units of its worst-case
+rounding bound u (|G| + E + 2^-14) is at most 2 everywhere, and its rms at
+most the rms of the statistical bound (u / sqrt 3) S (E and S from the
+oracle's error-scale functions).  Run on the oracle's own O and LSE (rounded
+to fp16 and fp32, as the forward hands them over), delta must also meet its
+definition dO . O for that O within the fp32 bound.  Cases: odd N at every supported head dim, causal
 and not; batch x heads with a ragged tail; the reference shape
 [4,32,2048,64] and [4,16,2048,128] (every element); long sequences, N = 8192
 (every element of two heads); stress inputs that move
@@ -18,8 +21,9 @@ import pytest
 
 from exact_attention_fwd_amd.workloads import make_qkv, stress_inputs
 from oracle import attention_bwd_fp64
-from oracle.attention_bwd import attention_bwd_error_scale
-from parity import grad_diff, run_gpu_bwd, say
+from oracle import attention_fp64
+from oracle.attention_bwd import attention_bwd_error_scale, attention_bwd_error_std
+from parity import delta_contract, grad_diff, run_gpu_bwd, say
 
 pytestmark = pytest.mark.gpu
 
@@ -33,16 +37,28 @@ def _do(shape, seed):
     return make_qkv(*shape, 1.0, seed=seed + 7919)[0]
 
 
-def check_bwd(name, q, k, v, do, scale, causal):
-    got = run_gpu_bwd(q, k, v, do, scale, causal)
+def check_bwd(name, q, k, v, do, scale, causal, given_o=False):
+    """The GPU backward against the oracle.  given_o: run it on the oracle's
+    O and LSE (rounded as the forward stores them) instead of the GPU
+    forward's, and check delta against its definition for that O."""
+    o16 = lse32 = None
+    if given_o:
+        o_ref, l_ref = attention_fp64(q, k, v, scale, causal=causal)
+        o16, lse32 = o_ref.astype(np.float16), l_ref.astype(np.float32)
+    got = run_gpu_bwd(q, k, v, do, scale, causal, o=o16, lse=lse32)
     ref = attention_bwd_fp64(q, k, v, do, scale, causal=causal)
     esc = attention_bwd_error_scale(q, k, v, do, scale, causal=causal)
+    sd = attention_bwd_error_std(q, k, v, do, scale, causal=causal)
     msgs, ok = [], True
-    for label, g, r, e in zip(("dq", "dk", "dv", "delta"), got, ref, esc):
+    for label, g, r, e, sg in zip(("dq", "dk", "dv", "delta"), got, ref, esc, sd):
         assert np.all(np.isfinite(g.astype(np.float32))), f"{name}: {label} not finite"
-        dd = grad_diff(g, r, e)
+        dd = grad_diff(g, r, e, sg)
         msgs.append(f"{label} {dd}")
         ok &= dd.ok()
+    if given_o:
+        dc = delta_contract(got[3], do, o16)
+        msgs.append(f"delta vs dO.O {dc:.3f}")
+        ok &= dc <= 1.0
     say(f"[bwd parity] {name}: " + "; ".join(msgs))
     assert ok, f"{name}: " + "; ".join(msgs)
     return got
@@ -141,8 +157,28 @@ def test_guard_bands_untouched():
         assert torch.all(b[:guard] == 7) and torch.all(b[guard + n:] == 7)
     ref = attention_bwd_fp64(q, k, v, do, d ** -0.5, causal=True)
     esc = attention_bwd_error_scale(q, k, v, do, d ** -0.5, causal=True)
-    for g, r, e in zip((dq, dk, dv, delta), ref, esc):
-        assert grad_diff(g.cpu().numpy(), r, e).ok()
+    sd = attention_bwd_error_std(q, k, v, do, d ** -0.5, causal=True)
+    for g, r, e, sg in zip((dq, dk, dv, delta), ref, esc, sd):
+        assert grad_diff(g.cpu().numpy(), r, e, sg).ok()
+
+
+@pytest.mark.parametrize("d", BWD_HEAD_DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [17, 129, 300])
+def test_on_the_oracles_o_and_lse(n, d, causal):
+    """The backward's own arithmetic: O and LSE from the oracle, so the only
+    roundings are the backward's; delta checked against dO . O for that O."""
+    q, k, v = make_qkv(1, 2, n, d, 1.0, seed=n + 1)
+    check_bwd(f"given O: N={n} d={d} causal={causal}", q, k, v, _do(q.shape, n + 1), d ** -0.5,
+              causal, given_o=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_on_the_oracles_o_full_size(causal):
+    shape = (2, 16, 2048, 64)
+    q, k, v = make_qkv(*shape, 1.0, seed=0)
+    check_bwd(f"given O: {list(shape)} causal={causal}", q, k, v, _do(shape, 0), 0.125, causal,
+              given_o=True)
 
 
 def test_head_dim_256_is_rejected():
