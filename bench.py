@@ -5,9 +5,12 @@
                     [--impl fa2|fa1] [--batch-sweep]
 
 Without --warmup / --steps, W fills about 0.4 s and K about 0.25 s of
-launches (the GPU's clock needs ~0.1 s of load to settle; a short kernel
-timed from a cold start reads up to ~6 % slow); the JSON line reports the W
-and K actually run.
+launches; the JSON line reports the W and K actually run.  The GPU's clock
+dips after load begins: at [4,32,2048,64] the first ~6 launches (1.2 ms)
+run at ~175 us, launches from ~1.2 ms to ~8 ms at 200-225 us, and the clock
+settles after ~25 ms of load at ~163 us per launch.  A short run such as
+--warmup 5 --steps 20 (~5 ms of load) times exactly that dip and reads
+25-30 % below the settled rate; nothing here shortens or skips it.
 
 A step is one fa2_fwd call: the whole hot path (load Q, stream K/V tiles,
 two MFMA contractions, online softmax, normalised O and LSE) over one batch
@@ -168,7 +171,9 @@ def summarize_counters(directory: str) -> dict:
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
-    """Time the oracle on whole (b, h) heads, as many as fit ~budget_s."""
+    """Time the oracle on whole (b, h) heads, as many as fit ~budget_s (the
+    median of three runs), or on the sampled rows of a long workload (one
+    run)."""
     import numpy as np
 
     from exact_attention_fwd_amd.workloads import sample_rows
@@ -193,13 +198,70 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         n_heads = int(min(w.B * w.H, max(threads, budget_s * threads / one)))
         n_heads = max(1, n_heads)
         qf, kf, vf = (x.reshape(1, w.B * w.H, w.N, w.d)[:, :n_heads] for x in (q, k, v))
-        t0 = time.perf_counter()
-        attention_fp64(qf, kf, vf, w.scale, causal=w.causal, threads=threads)
-        dt = time.perf_counter() - t0
+        runs = []
+        for _ in range(3):   # whole-head workloads: the median of three runs
+            t0 = time.perf_counter()
+            attention_fp64(qf, kf, vf, w.scale, causal=w.causal, threads=threads)
+            runs.append(time.perf_counter() - t0)
+        dt = sorted(runs)[1]
         flops = n_heads * w.N * per_row_flops
-        sample = f"{n_heads} of {w.B * w.H} heads of {w.name}, every query row"
+        sample = (f"{n_heads} of {w.B * w.H} heads of {w.name}, every query row; median of 3 runs "
+                  f"({', '.join(f'{r:.3f}' for r in runs)} s)")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 3)}
+
+
+def measured_ceilings(torch, dev, seconds: float = 0.25) -> dict:
+    """The box's practical ceilings, measured with library kernels (run after
+    the timed region, so they cannot warm the GPU for it):
+    dense fp16 matmul TFLOP/s (torch.matmul, hipBLASLt, 8192^3, fp32
+    accumulation), device-to-device copy GB/s (bytes read + written) and a
+    read-only stream GB/s (torch.sum over 1 GiB of fp16)."""
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize(dev)
+        n = max(5, int(seconds / max(time.perf_counter() - t0, 1e-6)))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    g = torch.Generator(device=dev).manual_seed(0)
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.float16, generator=g)
+    b = torch.randn((n, n), device=dev, dtype=torch.float16, generator=g)
+    c = torch.empty((n, n), device=dev, dtype=torch.float16)
+    t_mm = timed(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 2, device=dev, dtype=torch.float16)
+    dst = torch.empty_like(src)
+    t_cp = timed(lambda: dst.copy_(src))
+    t_sum = timed(lambda: torch.sum(src, dtype=torch.float32))
+    # a memory-bound matrix-vector product reads the 1 GiB matrix once
+    mat = src.view(32768, 16384)
+    x = torch.ones(16384, device=dev, dtype=torch.float16)
+    y = torch.empty(32768, device=dev, dtype=torch.float16)
+    t_mv = timed(lambda: torch.mv(mat, x, out=y))
+    del src, dst, mat, x, y
+    return {"fp16_matmul_tflops": 2.0 * n ** 3 / t_mm / 1e12,
+            "copy_gbs": 2.0 * nbytes / t_cp / 1e9,
+            "read_gbs": nbytes / min(t_sum, t_mv) / 1e9,
+            "read_gbs_sum": nbytes / t_sum / 1e9, "read_gbs_mv": nbytes / t_mv / 1e9,
+            "how": "torch.matmul fp16 [8192x8192]x[8192x8192] (hipBLASLt); copy_ of 1 GiB fp16 "
+                   "(bytes read + written); read stream = the faster of torch.sum over and "
+                   "torch.mv with a [32768x16384] fp16 matrix of that 1 GiB; HIP events, after "
+                   "the timed region"}
 
 
 def bwd_flops(w) -> float:
@@ -375,6 +437,16 @@ def bench_decode(args, w, torch, fa2):
                                   "kind": "oracle", "sample": f"every row of {w.name}",
                                   "seconds": round(dt, 3)}
         log(f"[bench] cpu baseline {result['cpu_baseline']}")
+    if not args.no_ceiling:
+        ceil = measured_ceilings(torch, dev)
+        best = max(ceil["read_gbs"], ceil["copy_gbs"])
+        result["roofline"]["measured_ceiling"] = {
+            "value": round(best, 1), "unit": "GB/s",
+            "kind": "fastest library streaming kernel (copy_ read + write, torch.mv read)",
+            "frac": round(result["roofline"]["achieved"] / best, 4),
+            "copy_gbs": round(ceil["copy_gbs"], 1), "read_gbs": round(ceil["read_gbs"], 1),
+            "how": ceil["how"]}
+        log(f"[bench] measured ceilings {ceil}")
     print(json.dumps(result), flush=True)
 
 
@@ -393,6 +465,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured library ceilings (fp16 matmul, copy, read stream)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="instead: print only the measured library ceilings and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="instead: build profiles/traffic.json from rocprofv3 --pmc runs in DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -425,6 +501,13 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.ceiling:
+        ceil = measured_ceilings(torch, torch.device("cuda:0"), seconds=1.0)
+        ceil["fp16_matmul_frac_of_peak"] = ceil["fp16_matmul_tflops"] / PEAK_FP16_TFLOPS
+        ceil["read_frac_of_peak"] = ceil["read_gbs"] / PEAK_HBM_GBS
+        print(json.dumps(ceil), flush=True)
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -602,6 +685,16 @@ def main():
         result["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_budget) if args.which == "fwd"
                                   else cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget))
         log(f"[bench] cpu baseline {result['cpu_baseline']}")
+
+    if not args.no_ceiling:
+        ceil = measured_ceilings(torch, dev)
+        result["roofline"]["measured_ceiling"] = {
+            "value": round(ceil["fp16_matmul_tflops"], 1), "unit": "TFLOP/s",
+            "kind": "dense fp16 matmul (hipBLASLt)",
+            "frac": round(result["roofline"]["achieved"] / ceil["fp16_matmul_tflops"], 4),
+            "copy_gbs": round(ceil["copy_gbs"], 1), "read_gbs": round(ceil["read_gbs"], 1),
+            "how": ceil["how"]}
+        log(f"[bench] measured ceilings {ceil}")
 
     print(json.dumps(result), flush=True)
 
