@@ -361,3 +361,104 @@ def test_large_scores_stay_finite():
     assert np.abs(lse).max() > 800
     p = attention_probs_fp64(q, k, 1.0, causal=True)
     np.testing.assert_allclose(p.sum(axis=-1), 1.0, atol=1e-12)
+
+
+# ------------------------------------------------ planted mistakes fail a pin
+def _mutant_rows():
+    """Plausible slips in the oracle's per-block step (each a replacement for
+    oracle.attention._attention_rows, same signature and returns)."""
+    import oracle.attention as oa
+
+    def scores(q_rows, row_ids, k, sigma, causal, shift=0):
+        s = sigma * (q_rows @ k.T)
+        if causal:
+            keys = np.arange(k.shape[0])
+            s[keys[None, :] > row_ids[:, None] + shift] = -np.inf
+        return s
+
+    def finish(s, v, weights=None):
+        m = s.max(axis=1)
+        p = np.exp(s - m[:, None]) if weights is None else weights(s, m)
+        l = p.sum(axis=1)
+        return (p @ v) / l[:, None], m + np.log(l), m, l
+
+    def causal_off_by_one(q_rows, row_ids, k, v, sigma, causal):
+        return finish(scores(q_rows, row_ids, k, sigma, causal, shift=1), v)
+
+    def wrong_operand(q_rows, row_ids, k, v, sigma, causal):
+        return finish(scores(q_rows, row_ids, k, sigma, causal), k)
+
+    def no_max_shift(q_rows, row_ids, k, v, sigma, causal):
+        s = scores(q_rows, row_ids, k, sigma, causal)
+        p = np.exp(s)
+        l = p.sum(axis=1)
+        return (p @ v) / l[:, None], np.log(l), np.zeros(len(l)), l
+
+    def lse_without_max(q_rows, row_ids, k, v, sigma, causal):
+        o, _, m, l = finish(scores(q_rows, row_ids, k, sigma, causal), v)
+        return o, np.log(l), m, l
+
+    def no_normaliser(q_rows, row_ids, k, v, sigma, causal):
+        o, lse, m, l = finish(scores(q_rows, row_ids, k, sigma, causal), v)
+        return o * l[:, None], lse, m, l
+
+    def biased_sum(q_rows, row_ids, k, v, sigma, causal):
+        s = scores(q_rows, row_ids, k, sigma, causal)
+        m = s.max(axis=1)
+        p = np.exp(s - m[:, None])
+        l = p.sum(axis=1) * (1 + 1e-6)
+        return (p @ v) / l[:, None], m + np.log(l), m, l
+
+    def missing_scale(q_rows, row_ids, k, v, sigma, causal):
+        return finish(scores(q_rows, row_ids, k, 1.0, causal), v)
+
+    def reversed_weights(q_rows, row_ids, k, v, sigma, causal):
+        def w(s, m):
+            p = np.exp(np.where(np.isfinite(s), m[:, None] - s, -np.inf))
+            return p
+        return finish(scores(q_rows, row_ids, k, sigma, causal), v, w)
+
+    return oa, [causal_off_by_one, wrong_operand, no_max_shift, lse_without_max,
+                no_normaliser, biased_sum, missing_scale, reversed_weights]
+
+
+def _failed_pins(golden_dir):
+    """Run a set of the pins above; return the names of those that fail."""
+    pins = [
+        ("worked example", lambda: test_worked_example_full_softmax(golden_dir)),
+        ("causal row 0", test_causal_row_zero_sees_only_key_zero),
+        ("fp32 scale", test_scale_is_the_fp32_value),
+        ("large scores", test_large_scores_stay_finite),
+        ("brute force", lambda: [test_against_pure_python_brute_force(5, 2, c) for c in (False, True)]),
+        ("convex hull", lambda: [test_output_in_convex_hull_and_lse_bounds(c) for c in (False, True)]),
+    ]
+    failed = []
+    for name, pin in pins:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+def test_planted_mistakes_fail_a_pin(golden_dir, monkeypatch):
+    """Each plausible slip in the oracle's block step -- causal off by one,
+    the wrong operand in the second product, no max shift, the LSE without
+    m, no normalisation, a biased row sum, the scale left out, weights
+    reversed -- and the scale taken in fp64 instead of the fp32 value fail
+    at least one pin; the unmodified oracle fails none."""
+    assert _failed_pins(golden_dir) == []
+    oa, mutants = _mutant_rows()
+    good = oa._attention_rows
+    for bad in mutants:
+        monkeypatch.setattr(oa, "_attention_rows", bad)
+        failed = _failed_pins(golden_dir)
+        monkeypatch.setattr(oa, "_attention_rows", good)
+        assert failed, bad.__name__
+    good_sigma = oa._sigma
+    monkeypatch.setattr(oa, "_sigma", lambda scale: float(scale))
+    failed = _failed_pins(golden_dir)
+    monkeypatch.setattr(oa, "_sigma", good_sigma)
+    assert failed, "fp64 scale"
