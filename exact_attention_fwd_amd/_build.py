@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa2.so")
-SOURCES = [os.path.join(CSRC, "fa2_api.cpp"), os.path.join(CSRC, "fa2_fwd_gfx950.hip"),
+SOURCES = [os.path.join(CSRC, "fa2_api.cpp"), os.path.join(CSRC, "fa2_plan.cpp"),
+           os.path.join(CSRC, "fa2_fwd_gfx950.hip"),
            os.path.join(CSRC, "fa2_bwd_gfx950.hip"), os.path.join(CSRC, "fa1_fwd_gfx950.hip"),
            os.path.join(CSRC, "fa2_splitkv_gfx950.hip")]
 HIP_FLAGS = [

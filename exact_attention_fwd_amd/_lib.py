@@ -10,7 +10,10 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+# The in-tree build; FA2_LIBRARY names another build of the same C ABI (the
+# CPU tests use it for a sanitizer build of the argument checks).
+LIB_PATH = os.environ.get("FA2_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
 
 FA2_OK = 0
 FA2_ERR_INVALID_ARG = 1

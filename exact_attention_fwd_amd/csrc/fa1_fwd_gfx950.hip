@@ -261,8 +261,6 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 
 }  // namespace
 
-size_t fa1_workspace_floats(int BH, int N, int d) { return size_t(BH) * N * (size_t(d) + 2); }
-
 hipError_t launch_fa1(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
                       int BH, int N, int d, float scale, bool causal, hipStream_t stream) {
     // Scale handling as in the FA2 forward: |scale| below the smallest normal

@@ -343,27 +343,6 @@ hipError_t noalloc_scratch(hipStream_t stream, void** out) {
     return hipSuccess;
 }
 
-SplitPlan plan_splits(int BH, int Nq, int Nk, int requested) {
-    const int n_tk = (Nk + kBK - 1) / kBK;
-    const int n_qt = (Nq + kQW - 1) / kQW;
-    int n = requested;
-    if (n <= 0) {
-        // One workgroup per CU (256): measured best for d = 64 and 128 at
-        // 32..256 heads and 8K..128K keys -- every workgroup does the same
-        // work, so a second round only adds a tail.  Every split keeps at
-        // least one 64-key tile per wave (four).
-        const long target = 256;
-        const long groups = long(BH) * n_qt;
-        n = int(std::min<long>((target + groups - 1) / groups, std::max(1, n_tk / 4)));
-    }
-    n = std::max(1, std::min(n, n_tk));
-    const int tps = (n_tk + n - 1) / n;
-    SplitPlan p;
-    p.tiles_per_split = tps;
-    p.n_splits = (n_tk + tps - 1) / tps;   // no empty split
-    return p;
-}
-
 hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                           void* ws, int BH, int Nq, int Nk, int d, float scale,
                           const SplitPlan& plan, hipStream_t stream) {
