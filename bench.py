@@ -320,6 +320,127 @@ def time_calls(step, sync, warmup=None, steps=None):
     return steps, warmup, (time.perf_counter() - t0) / steps
 
 
+def _load_fwd(path):
+    """fa2_fwd of a library build at ``path`` (its own handle)."""
+    import ctypes
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    lib.fa2_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.fa2_fwd.restype = ctypes.c_int
+    return lib
+
+
+def tile_sweep_configs(d: int, causal: bool):
+    """The forward's compile-time tile choices worth timing at head dim d:
+    waves per workgroup (4 or 8 where the row's chunks divide evenly), K/V
+    tiles in LDS per tensor (2 or 4; 2 at d = 256), LDS operand reads ahead
+    of the MFMAs (3, 4, 5) and, in 8-wave groups, the raised priority of the
+    younger half (on, off).  Each is a dict of the FA2_FWD_* macros."""
+    out = []
+    for waves in ((4, 8) if d in (64, 128) else (0,)):
+        for bufs in ((2, 4) if d != 256 else (2,)):
+            for ahead in (3, 4, 5):
+                for prio in ((1, 0) if waves == 8 else (1,)):
+                    out.append({"FA2_FWD_WAVES": waves, "FA2_FWD_KV_BUFS": bufs,
+                                "FA2_FWD_AHEAD": ahead, "FA2_FWD_PRIO": prio})
+    return out
+
+
+def tile_sweep(args, w, torch):
+    """Offline sweep of the forward's tile choices: rebuild the library once
+    per configuration (parallel hipcc jobs into a temporary folder), check
+    each build's output bit for bit against the in-tree one, and time them
+    in interleaved rounds (HIP events, each round ~0.3 s of warm-up and
+    ~0.2 s timed per configuration, the order reversed every other round)."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    import exact_attention_fwd_amd as fa2
+    from exact_attention_fwd_amd import _build
+    from exact_attention_fwd_amd.workloads import make_qkv
+
+    cfgs = tile_sweep_configs(w.d, w.causal)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.sigma, w.seed)
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    with tempfile.TemporaryDirectory() as td:
+        def mk(i):
+            return _build.build(out=os.path.join(td, f"libfa2_{i}.so"),
+                                defines=tuple(f"{k}={v}" for k, v in cfgs[i].items()))
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            paths = list(ex.map(mk, range(len(cfgs))))
+        log(f"[sweep] built {len(paths)} libraries in {time.perf_counter() - t0:.0f} s")
+        libs = [_load_fwd(p) for p in paths]
+        ref_o, ref_l = fa2.fwd(tq, tk, tv, scale=w.scale, causal=w.causal)
+        outs = []
+        for lib in libs:
+            o = torch.empty_like(tq)
+            lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+            st = lib.fa2_fwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), w.B, w.H, w.N, w.d, w.scale, int(w.causal),
+                             stream.cuda_stream)
+            if st != fa2.FA2_OK:
+                raise RuntimeError(f"sweep build failed to launch: {fa2.fa2_status_string(st)}")
+            outs.append((o, lse))
+        torch.cuda.synchronize(dev)
+        same = [bool(torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
+                     and torch.equal(l.view(torch.int32), ref_l.view(torch.int32))) for o, l in outs]
+        times = [[] for _ in libs]
+        for r in range(args.sweep_rounds):
+            order = range(len(libs)) if r % 2 == 0 else reversed(range(len(libs)))
+            for i in order:
+                o, lse = outs[i]
+                a = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream.cuda_stream)
+
+                def step(lib=libs[i], a=a):
+                    lib.fa2_fwd(*a)
+                _, _, sec = time_calls(step, lambda: torch.cuda.synchronize(dev), warmup=None, steps=None)
+                times[i].append(sec)
+        flops = w.flops()
+        rows = []
+        for c, t, sm in zip(cfgs, times, same):
+            med = sorted(t)[len(t) // 2]
+            rows.append({**c, "ms": round(med * 1e3, 5), "tflops": round(flops / med / 1e12, 1),
+                         "runs_ms": [round(x * 1e3, 5) for x in t], "bit_identical": sm})
+        best = min(rows, key=lambda r: r["ms"])
+        print(json.dumps({"metric": "forward tile sweep, TFLOP/s per configuration", "workload": w.name,
+                          "configs": rows, "best": best}), flush=True)
+
+
+def split_sweep(args, w, torch, fa2):
+    """Split key/value forward of a decoding workload at each key-range
+    count: HBM GB/s of algorithmic bytes per count."""
+    from exact_attention_fwd_amd.workloads import make_decode_inputs
+
+    q, k, v = make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    out = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=dev)
+    auto = fa2.fa2_splitkv_splits(w.B, w.H, w.nq, w.N, w.d, 0)
+    points = []
+    for req in (1, 2, 4, 8, 16, 32, 64, 128, 0):
+        n = fa2.fa2_splitkv_splits(w.B, w.H, w.nq, w.N, w.d, req)
+        wsb = fa2.fa2_splitkv_workspace_bytes(w.B, w.H, w.nq, w.N, w.d, req)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        a = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+             ws.data_ptr(), wsb, w.B, w.H, w.nq, w.N, w.d, w.scale, req, stream.cuda_stream)
+
+        def step(a=a):
+            if fa2.fa2_fwd_splitkv(*a) != fa2.FA2_OK:
+                raise RuntimeError("fa2_fwd_splitkv failed")
+        _, _, sec = time_calls(step, lambda: torch.cuda.synchronize(dev))
+        points.append({"requested": req, "n_splits": n, "auto": req == 0, "us": round(sec * 1e6, 2),
+                       "gbs": round(w.hbm_bytes() / sec / 1e9, 1)})
+        log(f"[split-sweep] {points[-1]}")
+    print(json.dumps({"metric": "split key/value forward HBM GB/s per key-range count",
+                      "workload": w.name, "auto_splits": auto, "points": points}), flush=True)
+
+
 def batch_sweep(torch, fa2):
     """FA2 vs the FA1 loop order at [B, 32, 2048, 64], B = 1 .. 16."""
     from exact_attention_fwd_amd.workloads import make_qkv
@@ -462,6 +583,11 @@ def main():
                     help="forward implementation: fa2_fwd (default) or the FA1-order comparator")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="instead: FA2 vs FA1 order at [B,32,2048,64], B = 1..16, one JSON line")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="instead: rebuild and time the forward's tile choices on the workload")
+    ap.add_argument("--sweep-rounds", type=int, default=3, help="interleaved rounds of --tile-sweep")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="instead: time a decoding workload at each key-range count")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -529,6 +655,14 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.tile_sweep:
+        if w.Nq:
+            ap.error("--tile-sweep times the square forward; pick a non-decoding workload")
+        return tile_sweep(args, w, torch)
+    if args.split_sweep:
+        if not w.Nq:
+            ap.error("--split-sweep needs a decoding workload (decode_64k, decode_b8_8k)")
+        return split_sweep(args, w, torch, fa2)
     if w.Nq and (args.which != "fwd" or args.impl != "fa2"):
         ap.error(f"{w.name} is a decoding workload: it runs the split key/value forward only")
     if args.impl == "fa1" and (args.which != "fwd" or w.d != 64):

@@ -43,10 +43,15 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    """Build libfa2.so next to this file and return its path (always rebuilds)."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+def build(verbose: bool = False, resource_usage: bool = False, out: str | None = None,
+          defines: tuple = ()) -> str:
+    """Build libfa2.so next to this file (or at ``out``) and return its path
+    (always rebuilds).  ``defines`` are extra -D macros, e.g. the forward's
+    tuning knobs for a sweep build."""
+    dest = out or LIB_PATH
+    tmp = dest + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *[f"-D{d}" for d in defines], "-shared", "-I", INCLUDE, "-I", CSRC,
+           *SOURCES, "-o", tmp]
     if resource_usage:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,8 +61,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         raise RuntimeError(f"libfa2 build failed:\n{' '.join(cmd)}\n{log}")
     if verbose or resource_usage:
         print(log)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, dest)
+    return dest
 
 
 if __name__ == "__main__":

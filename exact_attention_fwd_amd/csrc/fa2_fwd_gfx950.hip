@@ -59,7 +59,8 @@
 //  * K and V tiles (64 keys) are double-buffered in LDS and staged through
 //    registers: each iteration writes the tiles fetched during the previous
 //    one and fetches the next with 128-bit buffer loads, one LDS store or one
-//    load per slot over the stream.  One barrier per tile.  In an 8-wave
+//    load per slot over the stream.  One barrier per tile (with the optional
+//    ring of four tiles per tensor, one per two tiles).  In an 8-wave
 //    workgroup the waves 4-7, which lose issue arbitration to the older waves
 //    0-3 on the same SIMD, run the stream at raised priority so the two
 //    halves reach the barrier closer together.
@@ -88,10 +89,25 @@ namespace {
 
 using namespace dev;
 
+// Compile-time tuning knobs.  The defaults are the measured choices;
+// `bench.py --tile-sweep` rebuilds the library with other values and times
+// them against each other.
+#ifndef FA2_FWD_WAVES        // waves per workgroup at d = 64, 96, 128 (4 or 8); 0: Cfg's choice
+#define FA2_FWD_WAVES 0
+#endif
+#ifndef FA2_FWD_KV_BUFS      // K/V tiles in LDS per tensor (2 or 4); 0: chosen at launch
+#define FA2_FWD_KV_BUFS 0
+#endif
+#ifndef FA2_FWD_AHEAD        // LDS operand reads in flight ahead of the MFMAs; 0: Cfg's choice
+#define FA2_FWD_AHEAD 0
+#endif
+#ifndef FA2_FWD_PRIO         // 8-wave groups: the younger half streams at raised priority
+#define FA2_FWD_PRIO 1
+#endif
+
 // A tile keeps the row's reference max while each lane's weights in it sum
 // to at most 2^kLazy, so every weight stays <= 2^8, far inside fp16 range.
 constexpr float kLazyBound = 256.0f;   // 2^kLazy, kLazy = 8
-constexpr int kAhead = 4;                // LDS operand reads in flight ahead of the MFMAs
 
 template <int D, bool CAUSAL>
 struct Cfg {
@@ -100,7 +116,10 @@ struct Cfg {
     // 6-7 % faster non-causal than two); one at d = 256, whose registers need
     // a SIMD each.
     static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
-    static constexpr int kWaves = (D == 128 || (D == 64 && !CAUSAL)) ? 8 : 4;
+    static constexpr int kWaves = (FA2_FWD_WAVES != 0 && (D == 64 || D == 128))
+                                      ? FA2_FWD_WAVES
+                                      : (D == 128 || (D == 64 && !CAUSAL)) ? 8 : 4;
+    static_assert(kWaves == 4 || kWaves == 8, "waves per workgroup");
     static constexpr int kWavesPerSimd = D == 256 ? 1 : D == 32 ? 3 : 2;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBQ = kWaves * kQW;               // query rows per workgroup
@@ -110,9 +129,30 @@ struct Cfg {
     static constexpr int kDSteps = D / 16;                 // k-steps of the S^T MFMA
     static constexpr int kDBlocks = D / 32;                // 32-row blocks of O^T
     static constexpr int kStage = kChunks / kWaves;        // staged chunks per thread per tile
+    static_assert(kChunks % kWaves == 0, "every chunk of a row staged by one wave");
     static constexpr int kPV = 4 * kDBlocks;               // P V MFMAs per tile
     static constexpr int kQK = 2 * kDSteps;                // S^T MFMAs per tile
     static constexpr int kSlots = kPV + kQK;               // one MFMA per slot
+    // LDS operand reads in flight ahead of the MFMAs (measured best: 5 at
+    // non-causal d = 64, 4 elsewhere; 3..5 lie within ~1 %).
+    static constexpr int kAhead = FA2_FWD_AHEAD != 0 ? FA2_FWD_AHEAD : (D == 64 && !CAUSAL) ? 5 : 4;
+    static_assert(kAhead >= 1 && kAhead <= 8, "read-ahead");
+    // K/V tiles in LDS per tensor: a ring of 2, or of 4, which needs a
+    // barrier only after every second tile (twice the LDS: 128 KiB at
+    // d = 128; too much at d = 256, and at d = 96 it keeps a second
+    // workgroup off the CU).  The launch picks the ring (pick_bufs);
+    // kRing4 says whether the ring of 4 is compiled at all.
+    static constexpr bool kRing4 = FA2_FWD_KV_BUFS == 4 ? (D != 96 && D != 256)
+                                 : FA2_FWD_KV_BUFS == 0 && ((D == 64 && !CAUSAL) || D == 128);
+    // Ring of 4 where measured faster (bench.py --tile-sweep, both run
+    // orders): non-causal d = 64 (+1.8 % at [4,32,2048,64]) and d = 128 once
+    // a workgroup's key loop is long (+1 % at [2,16,16384,128], +2.7 % at
+    // [1,16,65536,128] causal; -2 % at [4,32,2048,128]).
+    static int pick_bufs(int N) {
+        if (!kRing4) return 2;
+        if (FA2_FWD_KV_BUFS == 4) return 4;
+        return (D == 64 || N >= 8192) ? 4 : 2;
+    }
     // Element pairs enter the three-stage VALU chain (scaled score, exp2,
     // sum + fp16) in slots [kE0, kE1); a pair's last stage runs two slots
     // after its first.
@@ -133,7 +173,7 @@ struct Cfg {
     }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NB>
 __global__ __launch_bounds__((Cfg<D, CAUSAL>::kThreads))
 __attribute__((amdgpu_waves_per_eu(Cfg<D, CAUSAL>::kWavesPerSimd, Cfg<D, CAUSAL>::kWavesPerSimd)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
@@ -142,10 +182,10 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                     uint32_t q_and, uint32_t q_xor, int group) {
     using C = Cfg<D, CAUSAL>;
     static_assert(C::schedule_ok(), "P chunk rewritten before its last reader");
-    __shared__ __attribute__((aligned(16))) unsigned char kb0[C::kTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char kb1[C::kTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char vb0[C::kTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char vb1[C::kTileBytes];
+    static_assert(NB == 2 || NB == 4, "K/V buffers");
+    constexpr int kAhead = C::kAhead;
+    __shared__ __attribute__((aligned(16))) unsigned char kbuf[NB][C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NB][C::kTileBytes];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,27 +276,52 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         }
     };
 
-    // Prologue.  Both V buffers start zeroed: the first iteration's P V runs
-    // with P = 0 on buffer 1.  K(0), K(1) go to LDS; K(2) and V(0) are
-    // fetched for the first iteration to store.
-    for (int i = tid; i < C::kTileBytes / 16; i += C::kThreads) {
-        reinterpret_cast<u32x4*>(vb0)[i] = u32x4{0u, 0u, 0u, 0u};
-        reinterpret_cast<u32x4*>(vb1)[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    // Prologue.  The V buffer of tile -1 starts zeroed: the first
+    // iteration's P V runs with P = 0 on it.  With a ring of 4, K(0..2) and
+    // V(0) go to LDS and K(3), V(1) are fetched for the first iteration to
+    // store; with 2, K(0), K(1) go to LDS and K(2), V(0) are fetched.  All
+    // of these loads are issued together, before the first LDS store, so the
+    // workgroup waits for one memory round trip, not two.
+    for (int i = tid; i < C::kTileBytes / 16; i += C::kThreads)
+        reinterpret_cast<u32x4*>(vbuf[NB - 1])[i] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (NB == 4) {
+        u32x4 t0[C::kStage], t1[C::kStage], t2[C::kStage], t3[C::kStage];
 #pragma unroll
-    for (int j = 0; j < C::kStage; ++j) {
-        fetch1(stk[j], rK, 0, j);
-        fetch1(stv[j], rK, 1, j);
-    }
+        for (int j = 0; j < C::kStage; ++j) {
+            fetch1(t0[j], rK, 0, j);
+            fetch1(t1[j], rK, 1, j);
+            fetch1(t2[j], rK, 2, j);
+            fetch1(t3[j], rV, 0, j);
+        }
 #pragma unroll
-    for (int j = 0; j < C::kStage; ++j) {
-        put_k1(kb0, stk[j], j);
-        put_k1(kb1, stv[j], j);
-    }
+        for (int j = 0; j < C::kStage; ++j) {
+            fetch1(stk[j], rK, 3, j);
+            fetch1(stv[j], rV, 1, j);
+        }
 #pragma unroll
-    for (int j = 0; j < C::kStage; ++j) {
-        fetch1(stk[j], rK, 2, j);
-        fetch1(stv[j], rV, 0, j);
+        for (int j = 0; j < C::kStage; ++j) {
+            put_k1(kbuf[0], t0[j], j);
+            put_k1(kbuf[1], t1[j], j);
+            put_k1(kbuf[2], t2[j], j);
+            put_v1(vbuf[0], t3[j], j);
+        }
+    } else {
+        u32x4 t0[C::kStage], t1[C::kStage];
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            fetch1(t0[j], rK, 0, j);
+            fetch1(t1[j], rK, 1, j);
+        }
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            fetch1(stk[j], rK, 2, j);
+            fetch1(stv[j], rV, 0, j);
+        }
+#pragma unroll
+        for (int j = 0; j < C::kStage; ++j) {
+            put_k1(kbuf[0], t0[j], j);
+            put_k1(kbuf[1], t1[j], j);
+        }
     }
     __syncthreads();
     {   // S^T of tile 0
@@ -264,7 +329,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         for (int ds = 0; ds < C::kDSteps; ++ds) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const h8 a = *reinterpret_cast<const h8*>(kb0 + k_base + lds_k_off(2 * ds, 32 * kb));
+                const h8 a = *reinterpret_cast<const h8*>(kbuf[0] + k_base + lds_k_off(2 * ds, 32 * kb));
                 s0[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ds], ds == 0 ? f32x16{} : s0[kb], 0, 0, 0);
             }
         }
@@ -279,16 +344,22 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     }
     __syncthreads();   // K buffer 0 is free before the first iteration refills it
 
-    // Iteration t (PAR = t & 1).  Buffers: K(t+1) and V(t-1) are read from
-    // the buffers of parity 1-PAR; K(t+2) and V(t), staged in registers, go
-    // to the buffers of parity PAR, freed by the last barrier.  Loads past
+    // Iteration t (PAR = t mod NB; tile x lives in buffer x mod NB).  It
+    // reads K(t+1) (for S^T of the next tile) and V(t-1) (for P V of the
+    // previous one).  Ring of 4: it stores K(t+3) and V(t+1), staged in
+    // registers during iteration t-1, and fetches K(t+4), V(t+2); a barrier
+    // follows every odd iteration, so a buffer is rewritten only after the
+    // barrier that follows its last read, and read only after the barrier
+    // that follows its store.  Ring of 2: it stores K(t+2), V(t), fetches
+    // K(t+3), V(t+1), and every iteration ends with a barrier.  Loads past
     // the last tile read zeros or data that is never used.
     auto step = [&](auto par_tag, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
         constexpr int PAR = decltype(par_tag)::value;
-        unsigned char* kb_store = PAR ? kb1 : kb0;
-        unsigned char* vb_store = PAR ? vb1 : vb0;
-        const unsigned char* kb_read = PAR ? kb0 : kb1;
-        const unsigned char* vb_read = PAR ? vb0 : vb1;
+        constexpr int kAheadK = NB == 4 ? 3 : 2, kAheadV = NB == 4 ? 1 : 0;
+        unsigned char* kb_store = kbuf[(PAR + kAheadK) % NB];
+        unsigned char* vb_store = vbuf[(PAR + kAheadV) % NB];
+        const unsigned char* kb_read = kbuf[(PAR + 1) % NB];
+        const unsigned char* vb_read = vbuf[(PAR + NB - 1) % NB];
 
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -370,7 +441,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 #pragma unroll
         for (int p = 0; p < kAhead; ++p) read(p);
         __builtin_amdgcn_sched_barrier(0);
-        if (C::kWaves == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
+        if (FA2_FWD_PRIO && C::kWaves == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int p = 0; p < C::kSlots; ++p) {
             if (p + kAhead < C::kSlots) read(p + kAhead);
@@ -381,9 +452,9 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             if (p % 2 == 0 && p / 2 >= C::kStage && p / 2 < 2 * C::kStage)
                 put_v1(vb_store, stv[p / 2 - C::kStage], p / 2 - C::kStage);
             const int q = p - 2 * C::kStage - 1;
-            if (q >= 0 && q % 2 == 0 && q / 2 < C::kStage) fetch1(stk[q / 2], rK, t + 3, q / 2);
+            if (q >= 0 && q % 2 == 0 && q / 2 < C::kStage) fetch1(stk[q / 2], rK, t + kAheadK + 1, q / 2);
             if (q >= 0 && q % 2 == 0 && q / 2 >= C::kStage && q / 2 < 2 * C::kStage)
-                fetch1(stv[q / 2 - C::kStage], rV, t + 1, q / 2 - C::kStage);
+                fetch1(stv[q / 2 - C::kStage], rV, t + kAheadV + 1, q / 2 - C::kStage);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -413,15 +484,27 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             alpha = 1.0f;
             lsum += part;
         }
-        __syncthreads();
+        if (NB == 2 || (PAR & 1)) __syncthreads();
     };
 
     int t = 0;
-    for (; t + 1 < n_kt; t += 2) {
-        step(std::integral_constant<int, 0>{}, t, s0, s1);
-        step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
+    if constexpr (NB == 4) {
+        for (; t + 3 < n_kt; t += 4) {
+            step(std::integral_constant<int, 0>{}, t, s0, s1);
+            step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
+            step(std::integral_constant<int, 2>{}, t + 2, s0, s1);
+            step(std::integral_constant<int, 3>{}, t + 3, s1, s0);
+        }
+        if (t < n_kt) step(std::integral_constant<int, 0>{}, t, s0, s1);
+        if (t + 1 < n_kt) step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
+        if (t + 2 < n_kt) step(std::integral_constant<int, 2>{}, t + 2, s0, s1);
+    } else {
+        for (; t + 1 < n_kt; t += 2) {
+            step(std::integral_constant<int, 0>{}, t, s0, s1);
+            step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
+        }
+        if (t < n_kt) step(std::integral_constant<int, 0>{}, t, s0, s1);
     }
-    if (t < n_kt) step(std::integral_constant<int, 0>{}, t, s0, s1);
 
     // P V of the last tile.
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -429,7 +512,9 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
     }
     {
-        const unsigned char* vb_read = ((n_kt - 1) & 1) ? vb1 : vb0;
+        // V(n_kt-1) was stored before the barrier that followed iteration
+        // n_kt-2 or n_kt-1 (or in the prologue).
+        const unsigned char* vb_read = vbuf[(n_kt - 1) % NB];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -468,10 +553,20 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     const int n_qtiles = (N + C::kBQ - 1) / C::kBQ;
     const int n_wg = n_qtiles * BH;
     const int group = CAUSAL ? causal_group(n_qtiles, n_wg, 4 * C::kWavesPerSimd / C::kWaves) : 1;
-    hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(C::kThreads), 0, stream,
-                       static_cast<const _Float16*>(q), static_cast<const _Float16*>(k),
-                       static_cast<const _Float16*>(v), static_cast<_Float16*>(o), lse, N,
-                       n_qtiles, n_wg, c, q_and, q_xor, group);
+    const auto* qh = static_cast<const _Float16*>(q);
+    const auto* kh = static_cast<const _Float16*>(k);
+    const auto* vh = static_cast<const _Float16*>(v);
+    auto* oh = static_cast<_Float16*>(o);
+    if constexpr (C::kRing4) {
+        if (C::pick_bufs(N) == 4) {
+            hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, 4>), dim3(n_wg), dim3(C::kThreads), 0,
+                               stream, qh, kh, vh, oh, lse, N, n_qtiles, n_wg, c, q_and, q_xor,
+                               group);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, 2>), dim3(n_wg), dim3(C::kThreads), 0, stream,
+                       qh, kh, vh, oh, lse, N, n_qtiles, n_wg, c, q_and, q_xor, group);
     return hipGetLastError();
 }
 

@@ -117,6 +117,22 @@ def test_odd_lengths(n, d, causal):
     check(f"N={n} d={d} causal={causal}", q, k, v, d ** -0.5, causal)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [8192 + 37, 8192 + 193])
+def test_long_ragged_d128(n, causal):
+    """From N = 8192 the d = 128 kernel keeps a ring of four K/V tiles per
+    tensor (one barrier per two tiles); ragged ends at both tile parities."""
+    q, k, v = make_qkv(1, 2, n, 128, 1.0, seed=n)
+    check(f"N={n} d=128 causal={causal}", q, k, v, 128 ** -0.5, causal)
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling"])
+def test_long_moving_max_d128(kind):
+    q, k, v = stress_inputs(kind, 1, 1, 8192 + 5, 128, seed=4)
+    for causal in (False, True):
+        check(f"stress {kind} N=8197 d=128 causal={causal}", q, k, v, 1.0, causal)
+
+
 @pytest.mark.parametrize("d", HEAD_DIMS)
 def test_batch_heads_and_ragged_tail_together(d):
     q, k, v = make_qkv(3, 5, 300, d, 1.0, seed=7)
