@@ -184,8 +184,15 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     static_assert(C::schedule_ok(), "P chunk rewritten before its last reader");
     static_assert(NB == 2 || NB == 4, "K/V buffers");
     constexpr int kAhead = C::kAhead;
-    __shared__ __attribute__((aligned(16))) unsigned char kbuf[NB][C::kTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NB][C::kTileBytes];
+    // One LDS block: NB K tiles, then NB V tiles; after the key loop the
+    // epilogue reuses it to restage O (kOutStride bytes per row).
+    constexpr int kOutStride = C::kRowBytes + 16;
+    constexpr int kLdsBytes = 2 * NB * C::kTileBytes > C::kWaves * kQW * kOutStride
+                                  ? 2 * NB * C::kTileBytes
+                                  : C::kWaves * kQW * kOutStride;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    const auto kbuf = reinterpret_cast<unsigned char (*)[C::kTileBytes]>(lds);
+    const auto vbuf = reinterpret_cast<unsigned char (*)[C::kTileBytes]>(lds + NB * C::kTileBytes);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -527,11 +534,16 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 
     // Epilogue: one normalisation, fp16 (RNE) O, natural-log LSE.  O^T
     // element (db, r) of this lane is row my_q, column 32*db + 8*(r/4) +
-    // 4*hi + r%4.
+    // 4*hi + r%4: written straight out, one instruction would cover 32 rows
+    // with 16 bytes each.  The wave's 32 x D block goes through LDS instead
+    // (rows kOutStride = 2*D + 16 bytes apart, so the 8-byte writes of a
+    // half-wave fall on distinct banks) and leaves as 128-bit stores of
+    // whole rows: 64 lanes cover 1 KiB of consecutive output.
     const float lt = pair_sum(lsum);
     const float inv = __builtin_amdgcn_rcpf(lt);
     const auto rO = make_rsrc(O + head, head_bytes);
-    const int o_base = my_q * C::kRowBytes + 8 * hi;
+    __syncthreads();   // every wave is done with the K/V tiles
+    unsigned char* ob = lds + wave * kQW * kOutStride;
 #pragma unroll
     for (int db = 0; db < C::kDBlocks; ++db) {
 #pragma unroll
@@ -539,9 +551,18 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             h4 out;
 #pragma unroll
             for (int k = 0; k < 4; ++k) out[k] = (_Float16)(oacc[db][4 * rr + k] * inv);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), rO,
-                                                  o_base + 64 * db + 16 * rr, 0, 0);
+            *reinterpret_cast<h4*>(ob + l32 * kOutStride + 64 * db + 16 * rr + 8 * hi) = out;
         }
+    }
+    // The block is read back by this wave only: its own LDS writes must have
+    // completed (lgkmcnt(0)); no other wave is involved.
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kQW * C::kChunks / 64; ++i) {
+        const int row = (i * 64 + lane) / C::kChunks, ch = (i * 64 + lane) % C::kChunks;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * kOutStride + 16 * ch);
+        __builtin_amdgcn_raw_buffer_store_b128(val, rO, (qw0 + row) * C::kRowBytes + 16 * ch, 0, 0);
     }
     if (hi == 0 && my_q < N) LSE[size_t(bh) * N + my_q] = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
 }
