@@ -71,9 +71,10 @@
 //    same XCD (dispatch is round-robin over the 8 XCDs) and share its L2;
 //    causal grids start with the longest rows, across small groups of heads.
 
-// LDS tile layouts (fa2_device.h): K chunk-major, V swizzled (chunk-major
-// with an XOR of the row) for the transposing reads.  Both keep every
-// per-lane address a lane base plus a compile-time offset.
+// LDS tile layouts (fa2_device.h): V swizzled (chunk-major with an XOR of the
+// row) for the transposing reads, K the same up to d = 128 and chunk-major at
+// d = 256.  Both keep every per-lane address a lane base plus a compile-time
+// offset.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -130,6 +131,9 @@ struct Cfg {
     static constexpr int kDBlocks = D / 32;                // 32-row blocks of O^T
     static constexpr int kStage = kChunks / kWaves;        // staged chunks per thread per tile
     static_assert(kChunks % kWaves == 0, "every chunk of a row staged by one wave");
+    // K/V staging in row blocks (contiguous global segments, swizzled K) up
+    // to d = 128; at d = 256 in chunk columns (see the kernel).
+    static constexpr bool kRowStage = D <= 128;
     static constexpr int kPV = 4 * kDBlocks;               // P V MFMAs per tile
     static constexpr int kQK = 2 * kDSteps;                // S^T MFMAs per tile
     static constexpr int kSlots = kPV + kQK;               // one MFMA per slot
@@ -235,18 +239,36 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Tiles below n_full need no mask for any row of the workgroup.
     const int n_full = CAUSAL ? min(N / kBK, (q0 + 1) / kBK) : N / kBK;
 
-    // Staging: thread (wave w, lane i) moves chunks w + kWaves*j (j < kStage) of
-    // key row i of a tile; the LDS address follows the tile's layout.
+    // Staging.  Load instruction n = w + kWaves*j (j < kStage) of wave w
+    // moves one block of a tile.  Row blocks (d <= 128): kRi row segments of
+    // kCi chunks -- 1 KiB of consecutive bytes when a row holds 8 or 16
+    // chunks -- each 16-lane group taking 4 rows x 4 chunks, so its LDS
+    // writes, both tiles in the swizzled layout, hit 16 distinct 16-byte bank
+    // groups.  Chunk columns (d = 256, whose registers have no room for the
+    // row block's addresses): chunk n of the 64 rows, one row per lane, K
+    // chunk-major.
     u32x4 stk[C::kStage], stv[C::kStage];
+    constexpr int kCi = (C::kChunks % 16 == 0) ? 16 : (C::kChunks % 8 == 0) ? 8 : 4;
+    constexpr int kRi = 64 / kCi;
+    constexpr int kCB = C::kChunks / kCi;
+    const int st_r = ((lane >> 4) % (kRi / 4)) * 4 + (lane & 3);
+    const int st_c = ((lane >> 4) / (kRi / 4)) * 4 + ((lane & 15) >> 2);
+    auto st_row = [&](int j) {
+        return C::kRowStage ? ((wave + C::kWaves * j) / kCB) * kRi + st_r : lane;
+    };
+    auto st_ch = [&](int j) {
+        return C::kRowStage ? ((wave + C::kWaves * j) % kCB) * kCi + st_c : wave + C::kWaves * j;
+    };
     auto fetch1 = [&](u32x4& dst, __amdgpu_buffer_rsrc_t r, int kt, int j) {
-        const int ch = wave + C::kWaves * j;
-        dst = __builtin_amdgcn_raw_buffer_load_b128(r, (kt * kBK + lane) * C::kRowBytes + ch * 16, 0, 0);
+        dst = __builtin_amdgcn_raw_buffer_load_b128(
+            r, (kt * kBK + st_row(j)) * C::kRowBytes + st_ch(j) * 16, 0, 0);
     };
     auto put_k1 = [&](unsigned char* buf, const u32x4& src, int j) {
-        *reinterpret_cast<u32x4*>(buf + lds_k_off(wave + C::kWaves * j, lane)) = src;
+        const int off = C::kRowStage ? lds_v_off(st_ch(j), st_row(j)) : lds_k_off(st_ch(j), st_row(j));
+        *reinterpret_cast<u32x4*>(buf + off) = src;
     };
     auto put_v1 = [&](unsigned char* buf, const u32x4& src, int j) {
-        *reinterpret_cast<u32x4*>(buf + lds_v_off(wave + C::kWaves * j, lane)) = src;
+        *reinterpret_cast<u32x4*>(buf + lds_v_off(st_ch(j), st_row(j))) = src;
     };
 
     f32x16 oacc[C::kDBlocks];
@@ -261,8 +283,14 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     f32x16 s0[2], s1[2];    // S^T of the even / odd tiles
 
     // Per-lane LDS read bases; the unrolled loops add compile-time offsets.
-    // K (A operand of S^T): key 32*kb + l32, chunk 2*ds + hi.
-    const int k_base = lds_k_off(hi, l32);
+    // K (A operand of S^T): key 32*kb + l32, chunk 2*ds + hi.  Swizzled K
+    // (row-block staging): chunk c of row r at (64c + (r ^ 4(c & 3))) * 16,
+    // and c & 3 = 2*(ds & 1) + hi, so two lane bases cover every (ds, kb).
+    const int k_base0 = C::kRowStage ? (hi * 64 + (l32 ^ (4 * hi))) << 4 : lds_k_off(hi, l32);
+    const int k_base1 = C::kRowStage ? (hi * 64 + (l32 ^ (8 + 4 * hi))) << 4 : k_base0;
+    auto k_off = [&](int ds, int kb) {
+        return ((ds & 1) ? k_base1 : k_base0) + lds_k_off(2 * ds, 32 * kb);
+    };
     // V^T (A operand of O^T) via ds_read_b64_tr_b16 (TrBase).
     const TrBase vt(lane);
 
@@ -336,7 +364,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         for (int ds = 0; ds < C::kDSteps; ++ds) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const h8 a = *reinterpret_cast<const h8*>(kbuf[0] + k_base + lds_k_off(2 * ds, 32 * kb));
+                const h8 a = *reinterpret_cast<const h8*>(kbuf[0] + k_off(ds, kb));
                 s0[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ds], ds == 0 ? f32x16{} : s0[kb], 0, 0, 0);
             }
         }
@@ -384,7 +412,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
                 ring[p % (kAhead + 1)] = read_tr_operand(vb_read, vt, tr_imm(ks, db));
             } else {
                 const int j = p - C::kPV, ds = j >> 1, kb = j & 1;
-                ring[p % (kAhead + 1)] = *reinterpret_cast<const h8*>(kb_read + k_base + lds_k_off(2 * ds, 32 * kb));
+                ring[p % (kAhead + 1)] = *reinterpret_cast<const h8*>(kb_read + k_off(ds, kb));
             }
         };
         auto mfma = [&](int p) {
