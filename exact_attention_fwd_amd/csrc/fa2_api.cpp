@@ -4,6 +4,7 @@
 // reported the same way on a machine without a GPU.
 #include "fa2.h"
 
+#include <cfloat>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -21,6 +22,15 @@ bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
     return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
+// A finite scale whose scores all stay finite in fp32: the largest score of
+// fp16 inputs is d * 65504^2, and the kernels form scale * log2(e) * score
+// (the exp2 argument) in fp32, so that product must not exceed FLT_MAX.
+bool scale_ok(float scale, int d) {
+    if (!std::isfinite(scale)) return false;
+    const double top = 1.4426950408889634 * 65504.0 * 65504.0 * double(d);
+    return std::fabs(double(scale)) * top <= double(FLT_MAX);
+}
+
 // Sizes, scale and head dim of the square-attention entry points (forward,
 // backward, FA1 order); 0 when valid.
 int check_sizes(int B, int H, int N, int d, float scale, int max_d) {
@@ -29,9 +39,9 @@ int check_sizes(int B, int H, int N, int d, float scale, int max_d) {
     // tiles of prefetch must stay below 2^31.
     if (N > (1 << 22)) return FA2_ERR_INVALID_ARG;
     if (int64_t(B) * H * N > INT32_MAX) return FA2_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return FA2_ERR_INVALID_ARG;
     if ((d != 32 && d != 64 && d != 96 && d != 128 && d != 256) || d > max_d)
         return FA2_ERR_UNSUPPORTED;
+    if (!scale_ok(scale, d)) return FA2_ERR_INVALID_ARG;
     if (int64_t(N) * d > (int64_t(1) << 29)) return FA2_ERR_INVALID_ARG;
     return 0;
 }
@@ -145,9 +155,9 @@ int check_splitkv_sizes(int B, int H, int Nq, int Nk, int d, float scale, int n_
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA2_ERR_INVALID_ARG;
     if (Nq > (1 << 22) || Nk > (1 << 22)) return FA2_ERR_INVALID_ARG;
     if (int64_t(B) * H * Nq > INT32_MAX || int64_t(B) * H * Nk > INT32_MAX) return FA2_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return FA2_ERR_INVALID_ARG;
     if (n_splits < 0 || n_splits > 4096) return FA2_ERR_INVALID_ARG;
     if (d != 32 && d != 64 && d != 96 && d != 128) return FA2_ERR_UNSUPPORTED;
+    if (!scale_ok(scale, d)) return FA2_ERR_INVALID_ARG;
     if (int64_t(Nq) * d > (int64_t(1) << 29) || int64_t(Nk) * d > (int64_t(1) << 29))
         return FA2_ERR_INVALID_ARG;
     return 0;

@@ -37,7 +37,7 @@ extern "C" {
 typedef enum {
     FA2_OK = 0,
     FA2_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, grid too large,
-                                non-finite scale, output aliasing an input     */
+                                non-finite or too large scale, output aliasing */
     FA2_ERR_UNSUPPORTED = 2, /* head dim not one of 32, 64, 96, 128, 256
                                 (fa2_bwd: 32, 64, 96, 128)                     */
     FA2_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned                  */
@@ -60,8 +60,12 @@ typedef enum {
  *   B, H, N : batch, heads, sequence length (queries = keys = N); each >= 1,
  *             N <= 4194304 (2^22), N * d <= 2^29 and B * H * N <= 2^31 - 1.
  *   d       : head dimension: 32, 64, 96, 128 or 256.
- *   scale   : softmax scale (normally 1/sqrt(d)); any finite value.  0 gives
- *             uniform weights over the visible keys.
+ *   scale   : softmax scale (normally 1/sqrt(d)); finite, with
+ *             |scale| * log2(e) * 65504^2 * d <= FLT_MAX (|scale| up to about
+ *             5.5e28 / d), so that every scaled score of fp16 inputs is a
+ *             finite fp32 number; larger or non-finite values are rejected
+ *             with FA2_ERR_INVALID_ARG.  0 gives uniform weights over the
+ *             visible keys.
  *   causal  : non-zero: query i sees keys j <= i only (top-left aligned).
  *   stream  : a hipStream_t passed as void*; NULL means the null stream.
  *

@@ -6,6 +6,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import exact_attention_fwd_amd as fa2
@@ -77,6 +78,33 @@ def test_too_many_rows(lib):
 @pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
 def test_non_finite_scale(lib, scale):
     assert call(scale=scale) == fa2.FA2_ERR_INVALID_ARG
+
+
+def _scale_limit(d):
+    """Largest |scale| whose scaled scores of fp16 inputs all stay finite in
+    fp32: |scale| * log2(e) * 65504^2 * d <= FLT_MAX."""
+    return float(np.finfo(np.float32).max) / (math.log2(math.e) * 65504.0 ** 2 * d)
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("sign", [1, -1])
+def test_scale_beyond_the_fp32_score_range(lib, d, sign):
+    lim = _scale_limit(d)
+    below = float(np.float32(lim * (1 - 2 ** -20)))
+    above = float(np.float32(lim * (1 + 2 ** -20)))
+    # a misaligned Q, checked after the scale rule, shows that the largest
+    # accepted scale passes it without reaching a HIP call
+    assert call(q=Q + 2, d=d, scale=sign * below) == fa2.FA2_ERR_MISALIGNED
+    assert call(d=d, scale=sign * above) == fa2.FA2_ERR_INVALID_ARG
+    assert call(d=d, scale=sign * 1e37) == fa2.FA2_ERR_INVALID_ARG
+    if d <= 128:
+        assert bcall(d=d, scale=sign * above) == fa2.FA2_ERR_INVALID_ARG
+        assert bcall(q=Q + 2, d=d, scale=sign * below) == fa2.FA2_ERR_MISALIGNED
+        assert scall(d=d, scale=sign * above) == fa2.FA2_ERR_INVALID_ARG
+        assert ncall(d=d, scale=sign * above) == fa2.FA2_ERR_INVALID_ARG
+        assert ncall(k=K + 8, d=d, scale=sign * below) == fa2.FA2_ERR_MISALIGNED
+    if d == 64:
+        assert fcall(scale=sign * above) == fa2.FA2_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("d", [0, 16, 48, 63, 80, 160, 192, 512])

@@ -157,6 +157,34 @@ def test_scale_values(scale):
         check(f"scale={scale} causal={causal}", q, k, v, scale, causal)
 
 
+@pytest.mark.parametrize("scale", [1e25, -1e25])
+def test_huge_scale_is_a_hard_argmax(scale):
+    """|scale| = 1e25 lies inside the accepted range at d = 64 (up to about
+    8.6e26): the softmax becomes a hard argmax, O is the V row of the best
+    key and LSE is scale times that key's score.  Rows whose two best scores
+    lie within what fp32 summation can move them are skipped."""
+    q, k, v = make_qkv(1, 2, 200, 64, 1.0, seed=11)
+    for causal in (False, True):
+        o, l = run_gpu(q, k, v, scale, causal)
+        assert np.all(np.isfinite(o.astype(np.float32))) and np.all(np.isfinite(l))
+        q64, k64 = q.astype(np.float64), k.astype(np.float64)
+        s = scale * np.einsum("bhid,bhjd->bhij", q64, k64)
+        mag = abs(scale) * np.einsum("bhid,bhjd->bhij", np.abs(q64), np.abs(k64))
+        if causal:
+            s = np.where(np.tril(np.ones(s.shape[-2:], bool)), s, -np.inf)
+        best = np.argmax(s, axis=-1)
+        top2 = np.sort(s, axis=-1)[..., -2:]
+        slack = 64 * 2.0 ** -24 * np.take_along_axis(mag, best[..., None], -1)[..., 0]
+        clear = (top2[..., 1] - top2[..., 0]) > 4 * slack
+        say(f"[parity] scale={scale:g} causal={causal}: {clear.mean():.3f} of the rows checked")
+        assert clear.mean() > 0.95
+        want_o = v[np.arange(1)[:, None, None], np.arange(2)[None, :, None], best]
+        assert np.array_equal(o[clear], want_o[clear])
+        want_l = top2[..., 1]
+        err = np.abs(l.astype(np.float64) - want_l)
+        assert np.all(err[clear] <= slack[clear] + 4 * 2.0 ** -24 * np.abs(want_l[clear]))
+
+
 # ----------------------------------------- full-size properties, every element
 @pytest.mark.parametrize("causal", [False, True])
 def test_full_size_closed_forms(causal):
