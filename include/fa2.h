@@ -65,7 +65,12 @@ typedef enum {
  *             5.5e28 / d), so that every scaled score of fp16 inputs is a
  *             finite fp32 number; larger or non-finite values are rejected
  *             with FA2_ERR_INVALID_ARG.  0 gives uniform weights over the
- *             visible keys.
+ *             visible keys.  Precision: each weight is exp2 of an fp32
+ *             argument whose absolute error is about 2^-24 times the
+ *             largest |scale * log2(e) * q.k| of the row; results keep their
+ *             accuracy while that magnitude stays below about 2^16, and
+ *             carry none once it passes 2^26 (a row may then come out as
+ *             zeros, infinities or NaN).
  *   causal  : non-zero: query i sees keys j <= i only (top-left aligned).
  *   stream  : a hipStream_t passed as void*; NULL means the null stream.
  *

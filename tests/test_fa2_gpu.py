@@ -140,6 +140,20 @@ def test_batch_heads_and_ragged_tail_together(d):
         check(f"[3,5,300,{d}] causal={causal}", q, k, v, d ** -0.5, causal)
 
 
+@pytest.mark.parametrize("kind,B,H,N,scale", [
+    ("random", 2, 160, 256, 0.125), ("random", 1, 300, 512, -0.125), ("random", 4, 72, 1024, 0.125),
+    ("rising", 2, 160, 256, 1.0), ("falling", 1, 300, 512, 1.0), ("large", 2, 160, 256, 0.125)])
+def test_many_units_per_workgroup(kind, B, H, N, scale):
+    """Grids of 320 to 1152 (Q tile, head) units, more than the chip runs at
+    once, with the row max moving (rising keys), fixed in the first tile
+    (falling), far beyond exp's range (large) and a negative scale."""
+    if kind == "random":
+        q, k, v = make_qkv(B, H, N, 64, 1.0, seed=N + H)
+    else:
+        q, k, v = stress_inputs(kind, B, H, N, 64, seed=N + H)
+    check(f"{kind} [{B},{H},{N},64] scale={scale}", q, k, v, scale, False)
+
+
 # ----------------------------------------------------------- stress inputs
 @pytest.mark.parametrize("kind", ["rising", "falling", "large", "const_v", "zero_q"])
 @pytest.mark.parametrize("d", HEAD_DIMS)
@@ -157,12 +171,14 @@ def test_scale_values(scale):
         check(f"scale={scale} causal={causal}", q, k, v, scale, causal)
 
 
-@pytest.mark.parametrize("scale", [1e25, -1e25])
-def test_huge_scale_is_a_hard_argmax(scale):
-    """|scale| = 1e25 lies inside the accepted range at d = 64 (up to about
-    8.6e26): the softmax becomes a hard argmax, O is the V row of the best
-    key and LSE is scale times that key's score.  Rows whose two best scores
-    lie within what fp32 summation can move them are skipped."""
+@pytest.mark.parametrize("scale", [1000.0, -1000.0])
+def test_sharp_softmax_is_a_hard_argmax(scale):
+    """|scale| = 1000 at d = 64 (scaled scores up to about 6e4, inside the
+    precision range the header states): the softmax is a hard argmax for
+    every row whose two best scores are apart by more than 30 / (|scale|
+    log2 e) -- the runner-up weight is then below 2^-30 -- so O is the V
+    row of the best key to fp16 rounding, and LSE is scale times that
+    key's score up to the fp32 rounding of the score."""
     q, k, v = make_qkv(1, 2, 200, 64, 1.0, seed=11)
     for causal in (False, True):
         o, l = run_gpu(q, k, v, scale, causal)
@@ -175,14 +191,16 @@ def test_huge_scale_is_a_hard_argmax(scale):
         best = np.argmax(s, axis=-1)
         top2 = np.sort(s, axis=-1)[..., -2:]
         slack = 64 * 2.0 ** -24 * np.take_along_axis(mag, best[..., None], -1)[..., 0]
-        clear = (top2[..., 1] - top2[..., 0]) > 4 * slack
+        clear = (top2[..., 1] - top2[..., 0]) * math.log2(math.e) > 30 + 4 * slack
         say(f"[parity] scale={scale:g} causal={causal}: {clear.mean():.3f} of the rows checked")
-        assert clear.mean() > 0.95
-        want_o = v[np.arange(1)[:, None, None], np.arange(2)[None, :, None], best]
-        assert np.array_equal(o[clear], want_o[clear])
+        assert clear.mean() > 0.9
+        want_o = v[np.arange(1)[:, None, None], np.arange(2)[None, :, None], best].astype(np.float32)
+        err_o = np.abs(o.astype(np.float32) - want_o)
+        # other weights sum to at most 200 * 2^-30 of the best one
+        assert np.all(err_o[clear] <= 2.0 ** -10 * np.abs(want_o[clear]) + 4e-6)
         want_l = top2[..., 1]
-        err = np.abs(l.astype(np.float64) - want_l)
-        assert np.all(err[clear] <= slack[clear] + 4 * 2.0 ** -24 * np.abs(want_l[clear]))
+        err_l = np.abs(l.astype(np.float64) - want_l)
+        assert np.all(err_l[clear] <= slack[clear] + 4 * 2.0 ** -24 * np.abs(want_l[clear]) + 1e-6)
 
 
 # ----------------------------------------- full-size properties, every element
