@@ -388,8 +388,12 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // that follows its store.  Ring of 2: it stores K(t+2), V(t), fetches
     // K(t+3), V(t+1), and every iteration ends with a barrier.  Loads past
     // the last tile read zeros or data that is never used.
-    auto step = [&](auto par_tag, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    auto step = [&](auto par_tag, auto last_tag, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
         constexpr int PAR = decltype(par_tag)::value;
+        // The last tile's iteration (LAST): there is no next tile, so it
+        // issues no S^T products and no fetches, and stores only what a later
+        // read needs.
+        constexpr bool LAST = decltype(last_tag)::value;
         constexpr int kAheadK = NB == 4 ? 3 : 2, kAheadV = NB == 4 ? 1 : 0;
         unsigned char* kb_store = kbuf[(PAR + kAheadK) % NB];
         unsigned char* vb_store = vbuf[(PAR + kAheadV) % NB];
@@ -479,17 +483,23 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         if (FA2_FWD_PRIO && C::kWaves == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int p = 0; p < C::kSlots; ++p) {
-            if (p + kAhead < C::kSlots) read(p + kAhead);
-            mfma(p);
+            if (p + kAhead < (LAST ? C::kPV : C::kSlots)) read(p + kAhead);
+            if (!LAST || p < C::kPV) mfma(p);
             __builtin_amdgcn_sched_barrier(0);
             valu(p);
-            if (p % 2 == 0 && p / 2 < C::kStage) put_k1(kb_store, stk[p / 2], p / 2);
-            if (p % 2 == 0 && p / 2 >= C::kStage && p / 2 < 2 * C::kStage)
-                put_v1(vb_store, stv[p / 2 - C::kStage], p / 2 - C::kStage);
-            const int q = p - 2 * C::kStage - 1;
-            if (q >= 0 && q % 2 == 0 && q / 2 < C::kStage) fetch1(stk[q / 2], rK, t + kAheadK + 1, q / 2);
-            if (q >= 0 && q % 2 == 0 && q / 2 >= C::kStage && q / 2 < 2 * C::kStage)
-                fetch1(stv[q / 2 - C::kStage], rV, t + kAheadV + 1, q / 2 - C::kStage);
+            // (With a ring of two the last iteration still stores V of its
+            // own tile, which the P V after the loop reads.)
+            if constexpr (!LAST || NB == 2) {
+                if (p % 2 == 0 && p / 2 >= C::kStage && p / 2 < 2 * C::kStage)
+                    put_v1(vb_store, stv[p / 2 - C::kStage], p / 2 - C::kStage);
+            }
+            if constexpr (!LAST) {
+                if (p % 2 == 0 && p / 2 < C::kStage) put_k1(kb_store, stk[p / 2], p / 2);
+                const int q = p - 2 * C::kStage - 1;
+                if (q >= 0 && q % 2 == 0 && q / 2 < C::kStage) fetch1(stk[q / 2], rK, t + kAheadK + 1, q / 2);
+                if (q >= 0 && q % 2 == 0 && q / 2 >= C::kStage && q / 2 < 2 * C::kStage)
+                    fetch1(stv[q / 2 - C::kStage], rV, t + kAheadV + 1, q / 2 - C::kStage);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -522,23 +532,59 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         if (NB == 2 || (PAR & 1)) __syncthreads();
     };
 
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using Mid = std::false_type;
+    using Last = std::true_type;
     int t = 0;
-    if constexpr (NB == 4) {
-        for (; t + 3 < n_kt; t += 4) {
-            step(std::integral_constant<int, 0>{}, t, s0, s1);
-            step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
-            step(std::integral_constant<int, 2>{}, t + 2, s0, s1);
-            step(std::integral_constant<int, 3>{}, t + 3, s1, s0);
+    // Up to d = 96 the last tile's iteration is a LAST step; at d = 128 and
+    // 256 its extra copy of the stream would cost registers (spills), so
+    // every iteration there is a full one.
+    const int n_main = n_kt - 1;   // iterations before the last tile's
+    if constexpr (D > 96) {
+        if constexpr (NB == 4) {
+            for (; t + 3 < n_kt; t += 4) {
+                step(I0{}, Mid{}, t, s0, s1);
+                step(I1{}, Mid{}, t + 1, s1, s0);
+                step(I2{}, Mid{}, t + 2, s0, s1);
+                step(I3{}, Mid{}, t + 3, s1, s0);
+            }
+            if (t < n_kt) step(I0{}, Mid{}, t, s0, s1);
+            if (t + 1 < n_kt) step(I1{}, Mid{}, t + 1, s1, s0);
+            if (t + 2 < n_kt) step(I2{}, Mid{}, t + 2, s0, s1);
+        } else {
+            for (; t + 1 < n_kt; t += 2) {
+                step(I0{}, Mid{}, t, s0, s1);
+                step(I1{}, Mid{}, t + 1, s1, s0);
+            }
+            if (t < n_kt) step(I0{}, Mid{}, t, s0, s1);
         }
-        if (t < n_kt) step(std::integral_constant<int, 0>{}, t, s0, s1);
-        if (t + 1 < n_kt) step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
-        if (t + 2 < n_kt) step(std::integral_constant<int, 2>{}, t + 2, s0, s1);
+    } else if constexpr (NB == 4) {
+        for (; t + 3 < n_main; t += 4) {
+            step(I0{}, Mid{}, t, s0, s1);
+            step(I1{}, Mid{}, t + 1, s1, s0);
+            step(I2{}, Mid{}, t + 2, s0, s1);
+            step(I3{}, Mid{}, t + 3, s1, s0);
+        }
+        if (t < n_main) step(I0{}, Mid{}, t, s0, s1);
+        if (t + 1 < n_main) step(I1{}, Mid{}, t + 1, s1, s0);
+        if (t + 2 < n_main) step(I2{}, Mid{}, t + 2, s0, s1);
+        switch (n_main & 3) {
+            case 0: step(I0{}, Last{}, n_main, s0, s1); break;
+            case 1: step(I1{}, Last{}, n_main, s1, s0); break;
+            case 2: step(I2{}, Last{}, n_main, s0, s1); break;
+            default: step(I3{}, Last{}, n_main, s1, s0); break;
+        }
     } else {
-        for (; t + 1 < n_kt; t += 2) {
-            step(std::integral_constant<int, 0>{}, t, s0, s1);
-            step(std::integral_constant<int, 1>{}, t + 1, s1, s0);
+        for (; t + 1 < n_main; t += 2) {
+            step(I0{}, Mid{}, t, s0, s1);
+            step(I1{}, Mid{}, t + 1, s1, s0);
         }
-        if (t < n_kt) step(std::integral_constant<int, 0>{}, t, s0, s1);
+        if (t < n_main) step(I0{}, Mid{}, t, s0, s1);
+        if (n_main & 1) step(I1{}, Last{}, n_main, s1, s0);
+        else step(I0{}, Last{}, n_main, s0, s1);
     }
 
     // P V of the last tile.
