@@ -388,12 +388,16 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // that follows its store.  Ring of 2: it stores K(t+2), V(t), fetches
     // K(t+3), V(t+1), and every iteration ends with a barrier.  Loads past
     // the last tile read zeros or data that is never used.
-    auto step = [&](auto par_tag, auto last_tag, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    auto step = [&](auto par_tag, auto kind_tag, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
         constexpr int PAR = decltype(par_tag)::value;
         // The last tile's iteration (LAST): there is no next tile, so it
         // issues no S^T products and no fetches, and stores only what a later
         // read needs.
-        constexpr bool LAST = decltype(last_tag)::value;
+        constexpr bool LAST = decltype(kind_tag)::value >= 1;
+        // DEAD (causal): every key of the last tile comes after every query
+        // of this wave, so its weights are all zero: only the P V of the
+        // previous tile remains.
+        constexpr bool DEAD = decltype(kind_tag)::value == 2;
         constexpr int kAheadK = NB == 4 ? 3 : 2, kAheadV = NB == 4 ? 1 : 0;
         unsigned char* kb_store = kbuf[(PAR + kAheadK) % NB];
         unsigned char* vb_store = vbuf[(PAR + kAheadV) % NB];
@@ -404,7 +408,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 #pragma unroll
             for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
         }
-        if (t >= n_full) mask_tile(t * kBK, s_cur);
+        if (!DEAD && t >= n_full) mask_tile(t * kBK, s_cur);
 
         // MFMA job p: p < kPV is P V (k-step p / kDBlocks, O^T block
         // p % kDBlocks), then S^T (d-step, key block).  Operands are read
@@ -486,7 +490,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             if (p + kAhead < (LAST ? C::kPV : C::kSlots)) read(p + kAhead);
             if (!LAST || p < C::kPV) mfma(p);
             __builtin_amdgcn_sched_barrier(0);
-            valu(p);
+            if constexpr (!DEAD) valu(p);
             // (With a ring of two the last iteration still stores V of its
             // own tile, which the P V after the loop reads.)
             if constexpr (!LAST || NB == 2) {
@@ -508,6 +512,9 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         // (The first weight of each partial sum starts it, no add of 0.)  Otherwise
         // (the row max moved up, or m2 was still -inf) take the recurrence
         // step exactly: m2 := max(m2, tile max), rescale, recompute.
+        if constexpr (DEAD) {
+            alpha = 1.0f;
+        } else {
         const float part = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
         if (__builtin_amdgcn_ballot_w64(!(part <= kLazyBound))) {
             float mx = -INFINITY;
@@ -529,6 +536,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             alpha = 1.0f;
             lsum += part;
         }
+        }
         if (NB == 2 || (PAR & 1)) __syncthreads();
     };
 
@@ -536,8 +544,11 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    using Mid = std::false_type;
-    using Last = std::true_type;
+    using Mid = std::integral_constant<int, 0>;
+    using Last = std::integral_constant<int, 1>;
+    using Dead = std::integral_constant<int, 2>;
+    // Causal: this wave's queries all come before the last tile's keys.
+    const bool dead = CAUSAL && qw0 + kQW <= (n_kt - 1) * kBK;
     int t = 0;
     // Up to d = 96 the last tile's iteration is a LAST step; at d = 128 and
     // 256 its extra copy of the stream would cost registers (spills), so
@@ -571,11 +582,20 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         if (t < n_main) step(I0{}, Mid{}, t, s0, s1);
         if (t + 1 < n_main) step(I1{}, Mid{}, t + 1, s1, s0);
         if (t + 2 < n_main) step(I2{}, Mid{}, t + 2, s0, s1);
-        switch (n_main & 3) {
-            case 0: step(I0{}, Last{}, n_main, s0, s1); break;
-            case 1: step(I1{}, Last{}, n_main, s1, s0); break;
-            case 2: step(I2{}, Last{}, n_main, s0, s1); break;
-            default: step(I3{}, Last{}, n_main, s1, s0); break;
+        if (CAUSAL && dead) {
+            switch (n_main & 3) {
+                case 0: step(I0{}, Dead{}, n_main, s0, s1); break;
+                case 1: step(I1{}, Dead{}, n_main, s1, s0); break;
+                case 2: step(I2{}, Dead{}, n_main, s0, s1); break;
+                default: step(I3{}, Dead{}, n_main, s1, s0); break;
+            }
+        } else {
+            switch (n_main & 3) {
+                case 0: step(I0{}, Last{}, n_main, s0, s1); break;
+                case 1: step(I1{}, Last{}, n_main, s1, s0); break;
+                case 2: step(I2{}, Last{}, n_main, s0, s1); break;
+                default: step(I3{}, Last{}, n_main, s1, s0); break;
+            }
         }
     } else {
         for (; t + 1 < n_main; t += 2) {
@@ -583,8 +603,13 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             step(I1{}, Mid{}, t + 1, s1, s0);
         }
         if (t < n_main) step(I0{}, Mid{}, t, s0, s1);
-        if (n_main & 1) step(I1{}, Last{}, n_main, s1, s0);
-        else step(I0{}, Last{}, n_main, s0, s1);
+        if (CAUSAL && dead) {
+            if (n_main & 1) step(I1{}, Dead{}, n_main, s1, s0);
+            else step(I0{}, Dead{}, n_main, s0, s1);
+        } else {
+            if (n_main & 1) step(I1{}, Last{}, n_main, s1, s0);
+            else step(I0{}, Last{}, n_main, s0, s1);
+        }
     }
 
     // P V of the last tile.
@@ -592,7 +617,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 #pragma unroll
         for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
     }
-    {
+    if (!dead) {
         // V(n_kt-1) was stored before the barrier that followed iteration
         // n_kt-2 or n_kt-1 (or in the prologue).
         const unsigned char* vb_read = vbuf[(n_kt - 1) % NB];
