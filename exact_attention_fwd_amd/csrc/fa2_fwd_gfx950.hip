@@ -226,13 +226,16 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Q^T fragments (B operand of S^T): lane holds query my_q, dims
     // 16*ds + 8*hi + [0,8).  q_and clears Q for a zero scale, q_xor flips its
     // sign for a negative one: softmax(s*S) = softmax(|s| * (-Q) K^T).
+    // Loaded in the prologue after the first K/V loads (load_q below).
     h8 qf[C::kDSteps];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int ds = 0; ds < C::kDSteps; ++ds) {
-        u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rQ, my_q * C::kRowBytes + 32 * ds + 16 * hi, 0, 0);
-        raw = (raw & q_and) ^ q_xor;
-        qf[ds] = __builtin_bit_cast(h8, raw);
-    }
+        for (int ds = 0; ds < C::kDSteps; ++ds) {
+            u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rQ, my_q * C::kRowBytes + 32 * ds + 16 * hi, 0, 0);
+            raw = (raw & q_and) ^ q_xor;
+            qf[ds] = __builtin_bit_cast(h8, raw);
+        }
+    };
 
     const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : N;
     const int n_kt = (kv_end + kBK - 1) / kBK;
@@ -316,7 +319,9 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // V(0) go to LDS and K(3), V(1) are fetched for the first iteration to
     // store; with 2, K(0), K(1) go to LDS and K(2), V(0) are fetched.  All
     // of these loads are issued together, before the first LDS store, so the
-    // workgroup waits for one memory round trip, not two.
+    // workgroup waits for one memory round trip, not two.  Q's loads come
+    // after the K/V ones: the LDS stores and the first barrier wait only for
+    // K/V (measured 0.6-2 % faster than Q first).
     for (int i = tid; i < C::kTileBytes / 16; i += C::kThreads)
         reinterpret_cast<u32x4*>(vbuf[NB - 1])[i] = u32x4{0u, 0u, 0u, 0u};
     if constexpr (NB == 4) {
@@ -333,6 +338,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             fetch1(stk[j], rK, 3, j);
             fetch1(stv[j], rV, 1, j);
         }
+        load_q();
 #pragma unroll
         for (int j = 0; j < C::kStage; ++j) {
             put_k1(kbuf[0], t0[j], j);
@@ -352,6 +358,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
             fetch1(stk[j], rK, 2, j);
             fetch1(stv[j], rV, 0, j);
         }
+        load_q();
 #pragma unroll
         for (int j = 0; j < C::kStage; ++j) {
             put_k1(kbuf[0], t0[j], j);
