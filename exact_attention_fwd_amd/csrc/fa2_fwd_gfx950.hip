@@ -60,7 +60,10 @@
 //    registers: each iteration writes the tiles fetched during the previous
 //    one and fetches the next with 128-bit buffer loads, one LDS store or one
 //    load per slot over the stream.  One barrier per tile (with the optional
-//    ring of four tiles per tensor, one per two tiles).  In an 8-wave
+//    ring of four tiles per tensor, one per two tiles).  Up to d = 96 the
+//    last tile's iteration is a shorter copy of the stream: no S^T of a next
+//    tile, no fetches; under the causal mask a wave whose queries all
+//    precede that tile also skips its (all-zero) softmax.  In an 8-wave
 //    workgroup the waves 4-7, which lose issue arbitration to the older waves
 //    0-3 on the same SIMD, run the stream at raised priority so the two
 //    halves reach the barrier closer together.
