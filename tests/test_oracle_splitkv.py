@@ -95,3 +95,71 @@ def test_merge_far_beyond_exp_range():
     np.testing.assert_allclose(l[0], 801.0 + np.log1p(np.exp(-1.0)), rtol=1e-15)
     o_e, l_e = merge_lse_fp64(np.zeros((2, 1, 3)), np.full((2, 1), -np.inf))
     assert np.all(o_e == 0) and np.all(l_e == -np.inf)
+
+
+# ------------------------------------------------ planted mistakes fail a pin
+def _merge_mutants():
+    good = merge_lse_fp64   # bound now: the pins see the mutant under this name
+
+    def no_max_shift(o_parts, lse_parts):
+        o, lse = np.asarray(o_parts, float), np.asarray(lse_parts, float)
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            w = np.exp(lse)
+            total = w.sum(axis=0)
+            return (w[..., None] * o).sum(axis=0) / total[..., None], np.log(total)
+
+    def lse_without_shift(o_parts, lse_parts):
+        o, l = good(o_parts, lse_parts)
+        m = np.asarray(lse_parts, float).max(axis=0)
+        return o, l - np.where(np.isfinite(m), m, 0.0)
+
+    def unnormalised_output(o_parts, lse_parts):
+        lse = np.asarray(lse_parts, float)
+        m = lse.max(axis=0)
+        shift = np.where(np.isfinite(m), m, 0.0)
+        w = np.exp(lse - shift)
+        o, l = good(o_parts, lse_parts)
+        return (w[..., None] * np.asarray(o_parts, float)).sum(axis=0), l
+
+    def max_instead_of_logsumexp(o_parts, lse_parts):
+        o, _ = good(o_parts, lse_parts)
+        return o, np.asarray(lse_parts, float).max(axis=0)
+
+    def reversed_weights(o_parts, lse_parts):
+        lse = np.asarray(lse_parts, float)
+        neg = good(o_parts, -lse)
+        return neg[0], good(o_parts, lse_parts)[1]
+
+    def plain_average(o_parts, lse_parts):
+        o, l = good(o_parts, lse_parts)
+        return np.asarray(o_parts, float).mean(axis=0), l
+
+    return [no_max_shift, lse_without_shift, unnormalised_output, max_instead_of_logsumexp,
+            reversed_weights, plain_average]
+
+
+def _failed_merge_pins(monkeypatch, bad):
+    import sys
+    mod = sys.modules[__name__]
+    monkeypatch.setattr(mod, "merge_lse_fp64", bad)
+    failed = []
+    pins = [lambda: test_merge_of_key_parts_is_the_full_attention([0, 17, 18, 33, 49, 50]),
+            lambda: test_merge_of_key_parts_is_the_full_attention([0, 25, 50]),
+            test_merge_invariants, test_merge_far_beyond_exp_range]
+    for i, pin in enumerate(pins):
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except AssertionError:
+            failed.append(i)
+    return failed
+
+
+def test_planted_mistakes_fail_a_pin(monkeypatch):
+    """Each plausible slip in the merge (no max shift, the shift dropped from
+    LSE, the output left unnormalised, max in place of log-sum-exp, reversed
+    weights, a plain average of the parts) fails at least one pin above; the
+    merge as written fails none."""
+    assert _failed_merge_pins(monkeypatch, merge_lse_fp64) == []
+    for bad in _merge_mutants():
+        assert _failed_merge_pins(monkeypatch, bad), bad.__name__
