@@ -525,27 +525,27 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         if constexpr (DEAD) {
             alpha = 1.0f;
         } else {
-        const float part = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
-        if (__builtin_amdgcn_ballot_w64(!(part <= kLazyBound))) {
-            float mx = -INFINITY;
+            const float part = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+            if (__builtin_amdgcn_ballot_w64(!(part <= kLazyBound))) {
+                float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) mx = __builtin_fmaxf(mx, sv(i));
-            const float m2_new = __builtin_fmaxf(m2, c * pair_max(mx));
-            const float sh = m2_new == -INFINITY ? 0.f : m2_new;
-            alpha = __builtin_amdgcn_exp2f(m2 - sh);
-            m2 = m2_new;
-            float r[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < 32; ++i) mx = __builtin_fmaxf(mx, sv(i));
+                const float m2_new = __builtin_fmaxf(m2, c * pair_max(mx));
+                const float sh = m2_new == -INFINITY ? 0.f : m2_new;
+                alpha = __builtin_amdgcn_exp2f(m2 - sh);
+                m2 = m2_new;
+                float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv(e), c, -sh));
-                r[e & 3] += pv;
-                pf[e >> 3][e & 7] = (_Float16)pv;
+                for (int e = 0; e < 32; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv(e), c, -sh));
+                    r[e & 3] += pv;
+                    pf[e >> 3][e & 7] = (_Float16)pv;
+                }
+                lsum = alpha * lsum + ((r[0] + r[1]) + (r[2] + r[3]));
+            } else {
+                alpha = 1.0f;
+                lsum += part;
             }
-            lsum = alpha * lsum + ((r[0] + r[1]) + (r[2] + r[3]));
-        } else {
-            alpha = 1.0f;
-            lsum += part;
-        }
         }
         if (NB == 2 || (PAR & 1)) __syncthreads();
     };
