@@ -17,10 +17,11 @@
 //
 //  * Each wave owns 32 whole query rows, so every row reduction stays inside
 //    the wave.  Head dims 32, 64, 96, 128 and 256 are compiled.  A workgroup
-//    is 8 waves (256 queries of one (batch, head)) at d = 128 and at
-//    non-causal d = 64, and 4 waves (128 queries) otherwise: 8 waves halve
-//    the K/V staging per query, while under the causal mask at d = 64 the
-//    smaller group wastes fewer masked keys on the diagonal.  Two waves share
+//    is 8 waves (256 queries of one (batch, head)) at d = 128 and at d = 64
+//    (causal d = 64: once N >= 2048 and the grid fills the chip), and 4
+//    waves (128 queries) otherwise: 8 waves halve the K/V staging per query,
+//    while the smaller group wastes fewer masked keys on the diagonal of
+//    short causal rows and fills the chip with small grids.  Two waves share
 //    each SIMD; three at d = 32, whose registers allow it; one at d = 256,
 //    where a wave's 32x256 fp32 accumulator needs the registers of a whole
 //    SIMD.
@@ -113,16 +114,16 @@ using namespace dev;
 // to at most 2^kLazy, so every weight stays <= 2^8, far inside fp16 range.
 constexpr float kLazyBound = 256.0f;   // 2^kLazy, kLazy = 8
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int WV = 0>
 struct Cfg {
     // Waves per workgroup (see the header): 8 at d = 128 and at non-causal
-    // d = 64, 4 otherwise.  Two waves per SIMD; three at d = 32 (measured
-    // 6-7 % faster non-causal than two); one at d = 256, whose registers need
-    // a SIMD each.
+    // d = 64, 4 otherwise; causal d = 64 has both shapes (WV), chosen at
+    // launch.  Two waves per SIMD; three at d = 32 (measured 6-7 % faster
+    // non-causal than two); one at d = 256, whose registers need a SIMD each.
     static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
-    static constexpr int kWaves = (FA2_FWD_WAVES != 0 && (D == 64 || D == 128))
-                                      ? FA2_FWD_WAVES
-                                      : (D == 128 || (D == 64 && !CAUSAL)) ? 8 : 4;
+    static constexpr int kWaves = (FA2_FWD_WAVES != 0 && (D == 64 || D == 128)) ? FA2_FWD_WAVES
+                                  : WV != 0                                    ? WV
+                                  : (D == 128 || (D == 64 && !CAUSAL))         ? 8 : 4;
     static_assert(kWaves == 4 || kWaves == 8, "waves per workgroup");
     static constexpr int kWavesPerSimd = D == 256 ? 1 : D == 32 ? 3 : 2;
     static constexpr int kThreads = 64 * kWaves;
@@ -141,8 +142,8 @@ struct Cfg {
     static constexpr int kQK = 2 * kDSteps;                // S^T MFMAs per tile
     static constexpr int kSlots = kPV + kQK;               // one MFMA per slot
     // LDS operand reads in flight ahead of the MFMAs (measured best: 5 at
-    // non-causal d = 64, 4 elsewhere; 3..5 lie within ~1 %).
-    static constexpr int kAhead = FA2_FWD_AHEAD != 0 ? FA2_FWD_AHEAD : (D == 64 && !CAUSAL) ? 5 : 4;
+    // 8-wave d = 64, 4 elsewhere; 3..5 lie within ~1 %).
+    static constexpr int kAhead = FA2_FWD_AHEAD != 0 ? FA2_FWD_AHEAD : (D == 64 && kWaves == 8) ? 5 : 4;
     static_assert(kAhead >= 1 && kAhead <= 8, "read-ahead");
     // K/V tiles in LDS per tensor: a ring of 2, or of 4, which needs a
     // barrier only after every second tile (twice the LDS: 128 KiB at
@@ -150,9 +151,9 @@ struct Cfg {
     // workgroup off the CU).  The launch picks the ring (pick_bufs);
     // kRing4 says whether the ring of 4 is compiled at all.
     static constexpr bool kRing4 = FA2_FWD_KV_BUFS == 4 ? (D != 96 && D != 256)
-                                 : FA2_FWD_KV_BUFS == 0 && ((D == 64 && !CAUSAL) || D == 128);
+                                 : FA2_FWD_KV_BUFS == 0 && ((D == 64 && kWaves == 8) || D == 128);
     // Ring of 4 where measured faster (bench.py --tile-sweep, both run
-    // orders): non-causal d = 64 (+1.8 % at [4,32,2048,64]) and d = 128 once
+    // orders): 8-wave d = 64 (+1.8 % at [4,32,2048,64]) and d = 128 once
     // a workgroup's key loop is long (+1 % at [2,16,16384,128], +2.7 % at
     // [1,16,65536,128] causal; -2 % at [4,32,2048,128]).
     static int pick_bufs(int N) {
@@ -180,14 +181,14 @@ struct Cfg {
     }
 };
 
-template <int D, bool CAUSAL, int NB>
-__global__ __launch_bounds__((Cfg<D, CAUSAL>::kThreads))
-__attribute__((amdgpu_waves_per_eu(Cfg<D, CAUSAL>::kWavesPerSimd, Cfg<D, CAUSAL>::kWavesPerSimd)))
+template <int D, bool CAUSAL, int NB, int WV>
+__global__ __launch_bounds__((Cfg<D, CAUSAL, WV>::kThreads))
+__attribute__((amdgpu_waves_per_eu(Cfg<D, CAUSAL, WV>::kWavesPerSimd, Cfg<D, CAUSAL, WV>::kWavesPerSimd)))
 void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__ K,
                     const _Float16* __restrict__ V, _Float16* __restrict__ O,
                     float* __restrict__ LSE, int N, int n_qtiles, int n_wg, float c,
                     uint32_t q_and, uint32_t q_xor, int group) {
-    using C = Cfg<D, CAUSAL>;
+    using C = Cfg<D, CAUSAL, WV>;
     static_assert(C::schedule_ok(), "P chunk rewritten before its last reader");
     static_assert(NB == 2 || NB == 4, "K/V buffers");
     constexpr int kAhead = C::kAhead;
@@ -676,10 +677,10 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     if (hi == 0 && my_q < N) LSE[size_t(bh) * N + my_q] = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                  int N, float c, uint32_t q_and, uint32_t q_xor, hipStream_t stream) {
-    using C = Cfg<D, CAUSAL>;
+template <int D, bool CAUSAL, int WV>
+hipError_t launch_w(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                    int N, float c, uint32_t q_and, uint32_t q_xor, hipStream_t stream) {
+    using C = Cfg<D, CAUSAL, WV>;
     const int n_qtiles = (N + C::kBQ - 1) / C::kBQ;
     const int n_wg = n_qtiles * BH;
     const int group = CAUSAL ? causal_group(n_qtiles, n_wg, 4 * C::kWavesPerSimd / C::kWaves) : 1;
@@ -689,15 +690,33 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     auto* oh = static_cast<_Float16*>(o);
     if constexpr (C::kRing4) {
         if (C::pick_bufs(N) == 4) {
-            hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, 4>), dim3(n_wg), dim3(C::kThreads), 0,
+            hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, 4, WV>), dim3(n_wg), dim3(C::kThreads), 0,
                                stream, qh, kh, vh, oh, lse, N, n_qtiles, n_wg, c, q_and, q_xor,
                                group);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, 2>), dim3(n_wg), dim3(C::kThreads), 0, stream,
+    hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, 2, WV>), dim3(n_wg), dim3(C::kThreads), 0, stream,
                        qh, kh, vh, oh, lse, N, n_qtiles, n_wg, c, q_and, q_xor, group);
     return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                  int N, float c, uint32_t q_and, uint32_t q_xor, hipStream_t stream) {
+    if constexpr (D == 64 && CAUSAL) {
+        // Causal d = 64: 8-wave groups (a ring of four, reads five ahead) once
+        // rows are long and the grid of 256-query tiles still gives every one
+        // of the 256 CUs a workgroup (measured +2 % at N = 2048, +4-5 % at
+        // 4096, +7-8 % at 16384 and 65536); 4-wave groups below (-3 % at
+        // N = 1024 with 8, -13 % at 512, and small grids leave CUs idle).
+        const int64_t n8 = int64_t((N + 255) / 256) * BH;
+        if (N >= 2048 && n8 >= 256)
+            return launch_w<D, CAUSAL, 8>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+        return launch_w<D, CAUSAL, 4>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+    } else {
+        return launch_w<D, CAUSAL, 0>(q, k, v, o, lse, BH, N, c, q_and, q_xor, stream);
+    }
 }
 
 }  // namespace
