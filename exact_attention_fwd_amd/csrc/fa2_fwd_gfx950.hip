@@ -142,10 +142,11 @@ struct Cfg {
     static constexpr int kQK = 2 * kDSteps;                // S^T MFMAs per tile
     static constexpr int kSlots = kPV + kQK;               // one MFMA per slot
     // LDS operand reads in flight ahead of the MFMAs (measured best: 5 at
-    // 8-wave d = 64, 3 at d = 128, 4 elsewhere; 3..5 lie within ~1 %).
-    static constexpr int kAhead = FA2_FWD_AHEAD != 0        ? FA2_FWD_AHEAD
-                                  : (D == 64 && kWaves == 8) ? 5
-                                  : D == 128                 ? 3 : 4;
+    // 8-wave d = 64 and at d = 256, 3 at d = 128, 4 elsewhere; 3..5 lie
+    // within ~1 %).
+    static constexpr int kAhead = FA2_FWD_AHEAD != 0                     ? FA2_FWD_AHEAD
+                                  : (D == 64 && kWaves == 8) || D == 256 ? 5
+                                  : D == 128                             ? 3 : 4;
     static_assert(kAhead >= 1 && kAhead <= 8, "read-ahead");
     // K/V tiles in LDS per tensor: a ring of 2, or of 4, which needs a
     // barrier only after every second tile (twice the LDS: 128 KiB at
