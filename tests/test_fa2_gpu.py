@@ -126,6 +126,27 @@ def test_long_ragged_d128(n, causal):
     check(f"N={n} d=128 causal={causal}", q, k, v, 128 ** -0.5, causal)
 
 
+@pytest.mark.parametrize("n,kind", [(2048, "random"), (4096 + 37, "random"), (2048, "rising"),
+                                    (4096 + 37, "falling")])
+def test_causal_d64_long_rows(n, kind):
+    """Causal d = 64 from N = 2048 on grids of >= 256 such workgroups runs
+    256-query workgroups with a ring of four K/V tiles (shorter rows: 128),
+    where waves whose queries all precede the last key tile skip its
+    softmax.  Ragged end included, and rows whose max rises with every key
+    tile (rising) or sits in the first (falling); 256 sampled rows per head,
+    the last rows among them."""
+    B, H = 1, 40
+    if kind == "random":
+        q, k, v = make_qkv(B, H, n, 64, 1.0, seed=n + 1)
+    else:
+        q, k, v = stress_inputs(kind, B, H, n, 64, seed=n + 1)
+    rows = np.stack([np.stack([np.unique(np.concatenate([sample_rows(n, b, h, 256),
+                                                         np.arange(n - 300, n)]))[-256:]
+                               if h % 2 else sample_rows(n, b, h, 256) for h in range(H)])
+                     for b in range(B)])
+    check(f"causal d=64 N={n} {kind}", q, k, v, 1.0 if kind != "random" else 0.125, True, rows=rows)
+
+
 @pytest.mark.parametrize("kind", ["rising", "falling"])
 def test_long_moving_max_d128(kind):
     q, k, v = stress_inputs(kind, 1, 1, 8192 + 5, 128, seed=4)
