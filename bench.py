@@ -264,6 +264,44 @@ def measured_ceilings(torch, dev, seconds: float = 0.25) -> dict:
                    "the timed region"}
 
 
+def lds_probe(torch, iters: int = 2000, reps: int = 20) -> dict:
+    """LDS read bandwidth of one CU for the forward's two LDS read
+    instructions (ds_read_b128 for K, ds_read_b64_tr_b16 for V) at 4, 8 and
+    16 waves per CU: one workgroup per CU, every wave reading a 64 KiB LDS
+    block over and over (libfa2probe.so).  Bytes per clock per CU use the
+    shader clock that wave 0 of workgroup 0 measured over its loop."""
+    import ctypes
+
+    from exact_attention_fwd_amd import _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        raise RuntimeError(f"{_build.PROBE_PATH} is not built (python -m exact_attention_fwd_amd._build)")
+    lib = ctypes.CDLL(_build.PROBE_PATH)
+    lib.fa2probe_lds_read.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    lib.fa2probe_lds_read.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    points = []
+    for mode, name in ((0, "ds_read_b128"), (1, "ds_read_b64_tr_b16")):
+        for waves in (4, 8, 16):
+            out = (ctypes.c_double * 3)()
+            rc = lib.fa2probe_lds_read(mode, 64 * waves, n_cu, iters, reps, out)
+            if rc != 0:
+                raise RuntimeError(f"fa2probe_lds_read({name}, {waves} waves) failed: {rc}")
+            ms, nbytes, ghz = out[0], out[1], out[2]
+            rate = nbytes / (ms * 1e-3)
+            points.append({"instruction": name, "waves_per_cu": waves, "ms": round(ms, 4),
+                           "tb_s": round(rate / 1e12, 2), "clock_ghz": round(ghz, 3),
+                           "bytes_per_clk_per_cu": round(rate / (ghz * 1e9) / n_cu, 1)})
+            log(f"[lds] {name} {waves} waves/CU: {rate / 1e12:.1f} TB/s at {ghz:.2f} GHz, "
+                f"{points[-1]['bytes_per_clk_per_cu']} B/clk/CU")
+    return {"metric": "LDS read bandwidth per CU", "unit": "bytes/clk/CU", "cus": n_cu,
+            "points": points,
+            "how": f"one workgroup of 64*waves threads per CU; each wave reads a 64 KiB LDS block "
+                   f"{iters} x 16 times (conflict-free consecutive lane segments); {reps} launches "
+                   f"timed with HIP events after 3 untimed; clock from s_memtime / s_memrealtime "
+                   f"of wave 0"}
+
+
 def bwd_flops(w) -> float:
     """10*B*H*N^2*d: S = Q K^T, dP = dO V^T, dV = P^T dO, dK = dS^T Q and
     dQ = dS K, 2*N^2*d each per head; halved when causal."""
@@ -597,6 +635,9 @@ def main():
                     help="instead: print only the measured library ceilings and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="instead: build profiles/traffic.json from rocprofv3 --pmc runs in DIR")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="instead: measure LDS read bandwidth per CU for ds_read_b128 and "
+                         "ds_read_b64_tr_b16 at 4, 8 and 16 waves per CU, print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -633,6 +674,10 @@ def main():
         ceil["fp16_matmul_frac_of_peak"] = ceil["fp16_matmul_tflops"] / PEAK_FP16_TFLOPS
         ceil["read_frac_of_peak"] = ceil["read_gbs"] / PEAK_HBM_GBS
         print(json.dumps(ceil), flush=True)
+        return
+
+    if args.lds_probe:
+        print(json.dumps(lds_probe(torch)), flush=True)
         return
 
     if args.copy_calibration:

@@ -39,6 +39,22 @@ def test_library_exports_every_declared_symbol(lib):
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
 
+def test_lds_probe_library_rejects_bad_arguments_before_any_hip_call():
+    # the measurement aid behind bench.py --lds-probe, a library of its own
+    if not os.path.exists(_build.PROBE_PATH):
+        _build.build_probe()
+    probe = ctypes.CDLL(_build.PROBE_PATH)
+    f = probe.fa2probe_lds_read
+    f.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    f.restype = ctypes.c_int
+    out = (ctypes.c_double * 3)()
+    assert f(2, 256, 1, 1, 1, out) == 1       # no such mode
+    assert f(0, 100, 1, 1, 1, out) == 1       # threads not whole waves
+    assert f(1, 2048, 1, 1, 1, out) == 1      # more than 1024 threads
+    assert f(0, 256, 0, 1, 1, out) == 1       # no workgroups
+    assert f(0, 256, 1, 1, 1, None) == 1      # no output
+
+
 def test_version_and_status_strings(lib):
     assert fa2.fa2_version().startswith("fa2-gfx950")
     seen = set()
