@@ -302,6 +302,39 @@ def lds_probe(torch, iters: int = 2000, reps: int = 20) -> dict:
                    f"of wave 0"}
 
 
+def valu_probe(torch, iters: int = 4000) -> dict:
+    """VALU issue rate (libfa2probe.so): shader-clock cycles per instruction
+    for 16 independent chains of v_add_f32, v_fma_f32, v_exp_f32, and the
+    mixes exp2 + add and exp2 + add + mul (cycles per group), at 1 to 4 waves
+    per SIMD (one workgroup of 256 to 1024 threads per CU)."""
+    import ctypes
+
+    from exact_attention_fwd_amd import _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        raise RuntimeError(f"{_build.PROBE_PATH} is not built (python -m exact_attention_fwd_amd._build)")
+    lib = ctypes.CDLL(_build.PROBE_PATH)
+    lib.fa2probe_valu_issue.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_double)]
+    lib.fa2probe_valu_issue.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    names = ("v_add_f32", "v_fma_f32", "v_exp_f32", "exp2+add", "exp2+add+mul")
+    points = []
+    for waves_per_simd in (1, 2, 3, 4):
+        for kind, name in enumerate(names):
+            out = (ctypes.c_double * 2)()
+            rc = lib.fa2probe_valu_issue(kind, 256 * waves_per_simd, n_cu, iters, out)
+            if rc != 0:
+                raise RuntimeError(f"fa2probe_valu_issue({name}, {waves_per_simd}) failed: {rc}")
+            points.append({"kind": name, "waves_per_simd": waves_per_simd,
+                           "cycles_per_wave": round(out[0], 2), "cycles_per_simd": round(out[1], 2)})
+            log(f"[valu] {name} {waves_per_simd} waves/SIMD: {out[0]:.2f} cycles per wave, "
+                f"{out[1]:.2f} per SIMD")
+    return {"metric": "VALU issue rate", "unit": "shader cycles per instruction (or group)",
+            "points": points,
+            "how": f"one workgroup per CU, 16 independent chains per wave, {iters} x 16 elements, "
+                   f"s_memtime around each wave's loop, averaged over every wave"}
+
+
 def bwd_flops(w) -> float:
     """10*B*H*N^2*d: S = Q K^T, dP = dO V^T, dV = P^T dO, dK = dS^T Q and
     dQ = dS K, 2*N^2*d each per head; halved when causal."""
@@ -638,6 +671,9 @@ def main():
     ap.add_argument("--lds-probe", action="store_true",
                     help="instead: measure LDS read bandwidth per CU for ds_read_b128 and "
                          "ds_read_b64_tr_b16 at 4, 8 and 16 waves per CU, print one JSON line")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="instead: measure the VALU issue rate (add, fma, exp2 and mixes) at 1 to 4 "
+                         "waves per SIMD, print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -678,6 +714,10 @@ def main():
 
     if args.lds_probe:
         print(json.dumps(lds_probe(torch)), flush=True)
+        return
+
+    if args.valu_probe:
+        print(json.dumps(valu_probe(torch)), flush=True)
         return
 
     if args.copy_calibration:

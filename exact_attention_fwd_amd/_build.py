@@ -2,8 +2,8 @@
 
     python -m exact_attention_fwd_amd._build [--resource-usage]
 
-It also builds libfa2probe.so (build_probe), the LDS bandwidth probe that
-bench.py --lds-probe runs; the attention library does not use it.
+It also builds libfa2probe.so (build_probe), the measurement probes that
+bench.py --lds-probe and --valu-probe run; the attention library does not use it.
 
 Every HIP translation unit is built for gfx950 only, with packed-FP32 ops
 disabled (the host pass warns that it does not know the feature; harmless).
@@ -68,13 +68,14 @@ def build(verbose: bool = False, resource_usage: bool = False, out: str | None =
     return dest
 
 
-PROBE_SOURCE = os.path.join(CSRC, "probe_lds_gfx950.hip")
+PROBE_SOURCE = os.path.join(CSRC, "probe_gfx950.hip")
 PROBE_PATH = os.path.join(PKG, "libfa2probe.so")
 
 
 def build_probe(verbose: bool = False) -> str:
-    """Build libfa2probe.so, the LDS bandwidth probe behind bench.py
-    --lds-probe (a measurement aid, separate from the attention library)."""
+    """Build libfa2probe.so, the LDS bandwidth and VALU issue probes behind
+    bench.py --lds-probe / --valu-probe (measurement aids, separate from the
+    attention library)."""
     tmp = PROBE_PATH + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", PROBE_SOURCE, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

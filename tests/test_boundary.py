@@ -39,8 +39,8 @@ def test_library_exports_every_declared_symbol(lib):
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
 
 
-def test_lds_probe_library_rejects_bad_arguments_before_any_hip_call():
-    # the measurement aid behind bench.py --lds-probe, a library of its own
+def test_probe_library_rejects_bad_arguments_before_any_hip_call():
+    # the measurement aids behind bench.py --lds-probe / --valu-probe, a library of their own
     if not os.path.exists(_build.PROBE_PATH):
         _build.build_probe()
     probe = ctypes.CDLL(_build.PROBE_PATH)
@@ -53,6 +53,12 @@ def test_lds_probe_library_rejects_bad_arguments_before_any_hip_call():
     assert f(1, 2048, 1, 1, 1, out) == 1      # more than 1024 threads
     assert f(0, 256, 0, 1, 1, out) == 1       # no workgroups
     assert f(0, 256, 1, 1, 1, None) == 1      # no output
+    g = probe.fa2probe_valu_issue
+    g.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_double)]
+    g.restype = ctypes.c_int
+    assert g(5, 256, 1, 1, out) == 1          # no such instruction kind
+    assert g(0, 96, 1, 1, out) == 1           # threads not whole waves
+    assert g(0, 256, 1, 0, out) == 1          # no iterations
 
 
 def test_version_and_status_strings(lib):
