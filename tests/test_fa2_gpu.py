@@ -147,6 +147,21 @@ def test_causal_d64_long_rows(n, kind):
     check(f"causal d=64 N={n} {kind}", q, k, v, 1.0 if kind != "random" else 0.125, True, rows=rows)
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(1, 4, 2048, True), (1, 32, 2048, True), (1, 8, 16384 + 37, False)])
+def test_d64_launch_shapes(B, H, N, causal):
+    """Each d = 64 launch choice at full size: causal rows of 2048 on a grid
+    too small for the 256-query groups (B*H = 4: 128-query groups, ring of
+    two), causal exactly at the boundary where the 256-query groups start
+    (B*H = 32: 256 of them), and long non-causal rows with a ragged end
+    (256-query groups, ring of four, 257 key tiles); 256 sampled rows per
+    head, the last rows among them."""
+    q, k, v = make_qkv(B, H, N, 64, 1.0, seed=N + H + B)
+    tail = np.arange(N - 64, N)
+    rows = np.stack([np.stack([np.sort(np.concatenate([np.setdiff1d(sample_rows(N, b, h, 256), tail)[:192],
+                                                       tail])) for h in range(H)]) for b in range(B)])
+    check(f"[{B},{H},{N},64] causal={causal}", q, k, v, 0.125, causal, rows=rows)
+
+
 @pytest.mark.parametrize("kind", ["rising", "falling"])
 def test_long_moving_max_d128(kind):
     q, k, v = stress_inputs(kind, 1, 1, 8192 + 5, 128, seed=4)
