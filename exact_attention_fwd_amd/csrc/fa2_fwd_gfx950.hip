@@ -61,10 +61,11 @@
 //    registers: each iteration writes the tiles fetched during the previous
 //    one and fetches the next with 128-bit buffer loads, one LDS store or one
 //    load per slot over the stream.  One barrier per tile (with the optional
-//    ring of four tiles per tensor, one per two tiles).  Up to d = 96 the
-//    last tile's iteration is a shorter copy of the stream: no S^T of a next
-//    tile, no fetches; under the causal mask a wave whose queries all
-//    precede that tile also skips its (all-zero) softmax.  In an 8-wave
+//    ring of four tiles per tensor, one per two tiles).  Up to d = 96, and at
+//    d = 128 with the ring of two, the last tile's iteration is a shorter
+//    copy of the stream: no S^T of a next tile, no fetches; under the causal
+//    mask a wave whose queries all precede that tile also skips its
+//    (all-zero) softmax.  In an 8-wave
 //    workgroup the waves 4-7, which lose issue arbitration to the older waves
 //    0-3 on the same SIMD, run the stream at raised priority so the two
 //    halves reach the barrier closer together.
@@ -564,11 +565,14 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     // Causal: this wave's queries all come before the last tile's keys.
     const bool dead = CAUSAL && qw0 + kQW <= (n_kt - 1) * kBK;
     int t = 0;
-    // Up to d = 96 the last tile's iteration is a LAST step; at d = 128 and
-    // 256 its extra copy of the stream would cost registers (spills), so
-    // every iteration there is a full one.
+    // Up to d = 96, and at d = 128 with the ring of two, the last tile's
+    // iteration is a LAST step (at d = 128 it reloads four spilled registers
+    // once per workgroup: unchanged non-causal, +0.7 to +1.7 % causal).  With
+    // the ring of four at d = 128, and at d = 256, its extra copy of the
+    // stream would spill hundreds of registers, so every iteration there is
+    // a full one.
     const int n_main = n_kt - 1;   // iterations before the last tile's
-    if constexpr (D > 96) {
+    if constexpr (D > 128 || (D == 128 && NB == 4)) {
         if constexpr (NB == 4) {
             for (; t + 3 < n_kt; t += 4) {
                 step(I0{}, Mid{}, t, s0, s1);
