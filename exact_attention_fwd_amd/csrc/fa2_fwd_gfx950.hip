@@ -428,18 +428,21 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         // MFMA job p: p < kPV is P V (k-step p / kDBlocks, O^T block
         // p % kDBlocks), then S^T (d-step, key block).  Operands are read
         // kAhead jobs early into a ring.
-        h8 ring[kAhead + 1];
+        // The last iteration at d = 128 reads only one product ahead: its
+        // extra copy of the stream then fits the registers (no spills).
+        constexpr int kA = (LAST && D == 128) ? kAhead - 2 : kAhead;
+        h8 ring[kA + 1];
         auto read = [&](int p) {
             if (p < C::kPV) {
                 const int ks = p / C::kDBlocks, db = p % C::kDBlocks;
-                ring[p % (kAhead + 1)] = read_tr_operand(vb_read, vt, tr_imm(ks, db));
+                ring[p % (kA + 1)] = read_tr_operand(vb_read, vt, tr_imm(ks, db));
             } else {
                 const int j = p - C::kPV, ds = j >> 1, kb = j & 1;
-                ring[p % (kAhead + 1)] = *reinterpret_cast<const h8*>(kb_read + k_off(ds, kb));
+                ring[p % (kA + 1)] = *reinterpret_cast<const h8*>(kb_read + k_off(ds, kb));
             }
         };
         auto mfma = [&](int p) {
-            const h8 a = ring[p % (kAhead + 1)];
+            const h8 a = ring[p % (kA + 1)];
             if (p < C::kPV) {
                 const int ks = p / C::kDBlocks, db = p % C::kDBlocks;
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], oacc[db], 0, 0, 0);
@@ -497,12 +500,12 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         // then their registers are refilled with K(t+3) and V(t+1) in the odd
         // slots after that.  The scheduling barriers keep this order.
 #pragma unroll
-        for (int p = 0; p < kAhead; ++p) read(p);
+        for (int p = 0; p < kA; ++p) read(p);
         __builtin_amdgcn_sched_barrier(0);
         if (FA2_FWD_PRIO && C::kWaves == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int p = 0; p < C::kSlots; ++p) {
-            if (p + kAhead < (LAST ? C::kPV : C::kSlots)) read(p + kAhead);
+            if (p + kA < (LAST ? C::kPV : C::kSlots)) read(p + kA);
             if (!LAST || p < C::kPV) mfma(p);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (!DEAD) valu(p);
@@ -566,11 +569,10 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     const bool dead = CAUSAL && qw0 + kQW <= (n_kt - 1) * kBK;
     int t = 0;
     // Up to d = 96, and at d = 128 with the ring of two, the last tile's
-    // iteration is a LAST step (at d = 128 it reloads four spilled registers
-    // once per workgroup: unchanged non-causal, +0.7 to +1.7 % causal).  With
-    // the ring of four at d = 128, and at d = 256, its extra copy of the
-    // stream would spill hundreds of registers, so every iteration there is
-    // a full one.
+    // iteration is a LAST step (+0.6 to +1.8 % causal at d = 128, 0 to +0.7 %
+    // non-causal).  With the ring of four at d = 128, and at d = 256, its
+    // extra copy of the stream would spill hundreds of registers, so every
+    // iteration there is a full one.
     const int n_main = n_kt - 1;   // iterations before the last tile's
     if constexpr (D > 128 || (D == 128 && NB == 4)) {
         if constexpr (NB == 4) {
