@@ -306,7 +306,9 @@ def valu_probe(torch, iters: int = 4000) -> dict:
     """VALU issue rate (libfa2probe.so): shader-clock cycles per instruction
     for 16 independent chains of v_add_f32, v_fma_f32, v_exp_f32, and the
     mixes exp2 + add and exp2 + add + mul (cycles per group), at 1 to 4 waves
-    per SIMD (one workgroup of 256 to 1024 threads per CU)."""
+    per SIMD (one workgroup of 256 to 1024 threads per CU).  A SIMD serves
+    its waves unevenly (the oldest runs ahead), so the per-SIMD rate comes
+    from the longest wave loop of each workgroup, not from the mean."""
     import ctypes
 
     from exact_attention_fwd_amd import _build
@@ -332,7 +334,48 @@ def valu_probe(torch, iters: int = 4000) -> dict:
     return {"metric": "VALU issue rate", "unit": "shader cycles per instruction (or group)",
             "points": points,
             "how": f"one workgroup per CU, 16 independent chains per wave, {iters} x 16 elements, "
-                   f"s_memtime around each wave's loop, averaged over every wave"}
+                   f"s_memtime around each wave's loop; per wave: the mean of the waves' loop "
+                   f"times; per SIMD: the longest loop of each workgroup's waves over the "
+                   f"elements per SIMD, mean over workgroups"}
+
+
+STEP_MODEL_MODES = ("mfma only", "sequential: S^T, softmax, P V", "pipelined, registers",
+                    "pipelined, operands from LDS", "pipelined, operands from LDS, barrier per 2 tiles",
+                    "sequential, operands from LDS")
+
+
+def step_probe(torch, iters: int = 4096, rounds: int = 2, reps: int = 3) -> dict:
+    """A ceiling for the d = 64 forward's key step (libfa2probe.so): per wave
+    the 16 MFMAs of one 64-key tile against 32 queries and the softmax VALU
+    work between them, with nothing loaded from HBM, in six variants that add
+    the kernel's parts one at a time (STEP_MODEL_MODES), at the waves per SIMD
+    the registers allow.  TFLOP/s count the MFMA work only, like the forward's
+    rate; one workgroup per CU, `rounds` workgroups per CU in turn."""
+    import ctypes
+
+    from exact_attention_fwd_amd import _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        raise RuntimeError(f"{_build.PROBE_PATH} is not built (python -m exact_attention_fwd_amd._build)")
+    lib = ctypes.CDLL(_build.PROBE_PATH)
+    lib.fa2probe_step_model.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    lib.fa2probe_step_model.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    points = []
+    for mode, name in enumerate(STEP_MODEL_MODES):
+        for w in range(1, (4 if mode <= 1 else 3 if mode in (2, 5) else 2) + 1):
+            out = (ctypes.c_double * 4)()
+            rc = lib.fa2probe_step_model(mode, w, n_cu * rounds, iters, reps, out)
+            if rc != 0:
+                raise RuntimeError(f"fa2probe_step_model({mode}, {w}) failed: {rc}")
+            points.append({"mode": name, "waves_per_simd": w, "ms": round(out[0], 4),
+                           "tflops": round(out[1], 1), "clock_ghz": round(out[2], 3),
+                           "mfma_busy": round(out[3], 3)})
+            log(f"[step] {name}, {w} waves/SIMD: {out[1]:.1f} TFLOP/s, {out[2]:.2f} GHz, "
+                f"MFMA busy {out[3]:.3f}")
+    return {"metric": "d = 64 key-step model", "unit": "TFLOP/s (MFMA work)", "points": points,
+            "how": f"{n_cu * rounds} workgroups of 256 x waves-per-SIMD threads, one per CU at a time, "
+                   f"{iters} tiles per wave, {reps} launches timed after one untimed"}
 
 
 def bwd_flops(w) -> float:
@@ -674,6 +717,9 @@ def main():
     ap.add_argument("--valu-probe", action="store_true",
                     help="instead: measure the VALU issue rate (add, fma, exp2 and mixes) at 1 to 4 "
                          "waves per SIMD, print one JSON line")
+    ap.add_argument("--step-probe", action="store_true",
+                    help="instead: time the register and LDS model of the d = 64 key step (MFMAs "
+                         "alone, sequential, pipelined, + LDS operands, + barriers), print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -718,6 +764,10 @@ def main():
 
     if args.valu_probe:
         print(json.dumps(valu_probe(torch)), flush=True)
+        return
+
+    if args.step_probe:
+        print(json.dumps(step_probe(torch)), flush=True)
         return
 
     if args.copy_calibration:

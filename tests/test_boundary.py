@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_probe_library_rejects_bad_arguments_before_any_hip_call():
-    # the measurement aids behind bench.py --lds-probe / --valu-probe, a library of their own
+    # the measurement aids behind bench.py --lds-probe / --valu-probe / --step-probe, a library of their own
     if not os.path.exists(_build.PROBE_PATH):
         _build.build_probe()
     probe = ctypes.CDLL(_build.PROBE_PATH)
@@ -59,6 +59,18 @@ def test_probe_library_rejects_bad_arguments_before_any_hip_call():
     assert g(5, 256, 1, 1, out) == 1          # no such instruction kind
     assert g(0, 96, 1, 1, out) == 1           # threads not whole waves
     assert g(0, 256, 1, 0, out) == 1          # no iterations
+    h = probe.fa2probe_step_model
+    h.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    h.restype = ctypes.c_int
+    out4 = (ctypes.c_double * 4)()
+    assert h(6, 1, 1, 2, 1, out4) == 1        # no such mode
+    assert h(2, 4, 1, 2, 1, out4) == 1        # four waves per SIMD do not fit the pipelined step
+    assert h(3, 3, 1, 2, 1, out4) == 1        # nor three with LDS operands
+    assert h(5, 4, 1, 2, 1, out4) == 1        # the sequential step with LDS operands: at most three
+    assert h(0, 0, 1, 2, 1, out4) == 1        # no waves
+    assert h(0, 1, 1, 3, 1, out4) == 1        # odd tile count
+    assert h(0, 1, 0, 2, 1, out4) == 1        # no workgroups
+    assert h(0, 1, 1, 2, 1, None) == 1        # no output
 
 
 def test_version_and_status_strings(lib):
