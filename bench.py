@@ -341,16 +341,44 @@ def valu_probe(torch, iters: int = 4000) -> dict:
 
 STEP_MODEL_MODES = ("mfma only", "sequential: S^T, softmax, P V", "pipelined, registers",
                     "pipelined, operands from LDS", "pipelined, operands from LDS, barrier per 2 tiles",
-                    "sequential, operands from LDS")
+                    "sequential, operands from LDS",
+                    "pipelined, LDS operands, barriers, K/V staged through registers",
+                    "pipelined, LDS operands, barriers, K/V staged by direct loads to LDS")
+
+
+def step_model_ceiling(torch, d: int, iters: int = 4096, reps: int = 3):
+    """TFLOP/s of the step model's full variant (K/V staged through registers,
+    two waves per SIMD, random operands) at head dim d, or None when the
+    probe library is not built."""
+    import ctypes
+
+    from exact_attention_fwd_amd import _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        log(f"[bench] {_build.PROBE_PATH} is not built: no step-model ceiling")
+        return None
+    lib = ctypes.CDLL(_build.PROBE_PATH)
+    lib.fa2probe_step_model.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_double)]
+    lib.fa2probe_step_model.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = (ctypes.c_double * 4)()
+    rc = lib.fa2probe_step_model(d, 6, 2, 1, n_cu * 2, iters, reps, out)
+    if rc != 0:
+        raise RuntimeError(f"fa2probe_step_model({d}) failed: {rc}")
+    return out[1]
 
 
 def step_probe(torch, iters: int = 4096, rounds: int = 2, reps: int = 3) -> dict:
-    """A ceiling for the d = 64 forward's key step (libfa2probe.so): per wave
-    the 16 MFMAs of one 64-key tile against 32 queries and the softmax VALU
-    work between them, with nothing loaded from HBM, in six variants that add
-    the kernel's parts one at a time (STEP_MODEL_MODES), at the waves per SIMD
-    the registers allow.  TFLOP/s count the MFMA work only, like the forward's
-    rate; one workgroup per CU, `rounds` workgroups per CU in turn."""
+    """A ceiling for the forward's key step at d = 64 and d = 128
+    (libfa2probe.so): per wave the MFMAs of one 64-key tile against 32
+    queries (d/4 of them) and the softmax VALU work between them, with
+    no output written, in variants that add the kernel's parts one at a time
+    (STEP_MODEL_MODES) up to the K/V staging from HBM, at the waves per SIMD
+    the registers allow; once with random fp16 operands like the forward's
+    N(0, 1) inputs and once with small smooth ones (the clock under an MFMA
+    load depends on the operand bits that toggle).
+    TFLOP/s count the MFMA work only, like the forward's rate; one workgroup
+    per CU, `rounds` workgroups per CU in turn."""
     import ctypes
 
     from exact_attention_fwd_amd import _build
@@ -358,22 +386,28 @@ def step_probe(torch, iters: int = 4096, rounds: int = 2, reps: int = 3) -> dict
     if not os.path.exists(_build.PROBE_PATH):
         raise RuntimeError(f"{_build.PROBE_PATH} is not built (python -m exact_attention_fwd_amd._build)")
     lib = ctypes.CDLL(_build.PROBE_PATH)
-    lib.fa2probe_step_model.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    lib.fa2probe_step_model.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_double)]
     lib.fa2probe_step_model.restype = ctypes.c_int
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    max_waves = {64: (4, 4, 3, 2, 2, 3, 2, 2), 128: (3, 3, 2, 2, 2, 2, 2, 2)}
     points = []
-    for mode, name in enumerate(STEP_MODEL_MODES):
-        for w in range(1, (4 if mode <= 1 else 3 if mode in (2, 5) else 2) + 1):
-            out = (ctypes.c_double * 4)()
-            rc = lib.fa2probe_step_model(mode, w, n_cu * rounds, iters, reps, out)
-            if rc != 0:
-                raise RuntimeError(f"fa2probe_step_model({mode}, {w}) failed: {rc}")
-            points.append({"mode": name, "waves_per_simd": w, "ms": round(out[0], 4),
-                           "tflops": round(out[1], 1), "clock_ghz": round(out[2], 3),
-                           "mfma_busy": round(out[3], 3)})
-            log(f"[step] {name}, {w} waves/SIMD: {out[1]:.1f} TFLOP/s, {out[2]:.2f} GHz, "
-                f"MFMA busy {out[3]:.3f}")
-    return {"metric": "d = 64 key-step model", "unit": "TFLOP/s (MFMA work)", "points": points,
+    for data in ("random", "smooth"):
+        for d in (64, 128):
+            for mode, name in enumerate(STEP_MODEL_MODES):
+                for w in range(1, max_waves[d][mode] + 1):
+                    if w == 1 and (mode >= 6 or (d == 128 and mode == 4)):
+                        continue
+                    out = (ctypes.c_double * 4)()
+                    rc = lib.fa2probe_step_model(d, mode, w, int(data == "random"), n_cu * rounds, iters,
+                                                 reps, out)
+                    if rc != 0:
+                        raise RuntimeError(f"fa2probe_step_model({d}, {mode}, {w}, {data}) failed: {rc}")
+                    points.append({"data": data, "d": d, "mode": name, "waves_per_simd": w,
+                                   "ms": round(out[0], 4), "tflops": round(out[1], 1),
+                                   "clock_ghz": round(out[2], 3), "mfma_busy": round(out[3], 3)})
+                    log(f"[step] {data} d={d} {name}, {w} waves/SIMD: {out[1]:.1f} TFLOP/s, "
+                        f"{out[2]:.2f} GHz, MFMA busy {out[3]:.3f}")
+    return {"metric": "key-step model", "unit": "TFLOP/s (MFMA work)", "points": points,
             "how": f"{n_cu * rounds} workgroups of 256 x waves-per-SIMD threads, one per CU at a time, "
                    f"{iters} tiles per wave, {reps} launches timed after one untimed"}
 
@@ -718,8 +752,9 @@ def main():
                     help="instead: measure the VALU issue rate (add, fma, exp2 and mixes) at 1 to 4 "
                          "waves per SIMD, print one JSON line")
     ap.add_argument("--step-probe", action="store_true",
-                    help="instead: time the register and LDS model of the d = 64 key step (MFMAs "
-                         "alone, sequential, pipelined, + LDS operands, + barriers), print one JSON line")
+                    help="instead: time the register and LDS model of the d = 64 and d = 128 key step "
+                         "(MFMAs alone, sequential, pipelined, + LDS operands, + barriers), print one "
+                         "JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
@@ -903,6 +938,21 @@ def main():
                      "launch_ms": round(ev_ms, 5)},
     }
 
+    # The model of the key step, timed right after the timed region so that the
+    # chip is in the same state (the clock under this load depends on it).
+    step_model = None
+    if (not args.no_ceiling and args.which == "fwd" and args.impl == "fa2" and not w.causal
+            and w.d in (64, 128)):
+        model = step_model_ceiling(torch, w.d)
+        if model is not None:
+            step_model = {
+                "value": round(model, 1), "unit": "TFLOP/s", "frac": round(achieved / model, 4),
+                "kind": f"the forward's key step at d = {w.d} alone (pipelined softmax, LDS operands, "
+                        f"barriers, K/V staging; random fp16 operands; no prologue or epilogue)",
+                "how": "bench.py --step-probe, last variant at two waves per SIMD, timed right after "
+                       "the timed region"}
+            log(f"[bench] step model {model:.1f} TFLOP/s")
+
     if args.which == "bwd":
         result["config"]["pass"] = "backward (dQ, dK, dV, delta)"
     if args.impl == "fa1":
@@ -964,6 +1014,8 @@ def main():
             "copy_gbs": round(ceil["copy_gbs"], 1), "read_gbs": round(ceil["read_gbs"], 1),
             "how": ceil["how"]}
         log(f"[bench] measured ceilings {ceil}")
+        if step_model is not None:
+            result["roofline"]["measured_ceiling"]["step_model"] = step_model
 
     print(json.dumps(result), flush=True)
 

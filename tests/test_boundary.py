@@ -60,17 +60,24 @@ def test_probe_library_rejects_bad_arguments_before_any_hip_call():
     assert g(0, 96, 1, 1, out) == 1           # threads not whole waves
     assert g(0, 256, 1, 0, out) == 1          # no iterations
     h = probe.fa2probe_step_model
-    h.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    h.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_double)]
     h.restype = ctypes.c_int
     out4 = (ctypes.c_double * 4)()
-    assert h(6, 1, 1, 2, 1, out4) == 1        # no such mode
-    assert h(2, 4, 1, 2, 1, out4) == 1        # four waves per SIMD do not fit the pipelined step
-    assert h(3, 3, 1, 2, 1, out4) == 1        # nor three with LDS operands
-    assert h(5, 4, 1, 2, 1, out4) == 1        # the sequential step with LDS operands: at most three
-    assert h(0, 0, 1, 2, 1, out4) == 1        # no waves
-    assert h(0, 1, 1, 3, 1, out4) == 1        # odd tile count
-    assert h(0, 1, 0, 2, 1, out4) == 1        # no workgroups
-    assert h(0, 1, 1, 2, 1, None) == 1        # no output
+    assert h(96, 0, 1, 1, 1, 2, 1, out4) == 1    # no model at this head dim
+    assert h(64, 8, 1, 1, 1, 2, 1, out4) == 1    # no such mode
+    assert h(64, 6, 1, 1, 1, 2, 1, out4) == 1    # the staging variants: two waves per SIMD only
+    assert h(128, 7, 3, 1, 1, 2, 1, out4) == 1
+    assert h(64, 2, 4, 1, 1, 2, 1, out4) == 1    # four waves per SIMD do not fit the pipelined step
+    assert h(64, 3, 3, 1, 1, 2, 1, out4) == 1    # nor three with LDS operands
+    assert h(64, 5, 4, 1, 1, 2, 1, out4) == 1    # the sequential step with LDS operands: at most three
+    assert h(128, 2, 3, 1, 1, 2, 1, out4) == 1   # d = 128 pipelined: at most two
+    assert h(128, 0, 4, 1, 1, 2, 1, out4) == 1   # d = 128 MFMAs alone: at most three
+    assert h(128, 4, 1, 1, 1, 2, 1, out4) == 1   # d = 128 with barriers: two only
+    assert h(64, 0, 1, 2, 1, 2, 1, out4) == 1    # operand data: 0 or 1
+    assert h(64, 0, 0, 1, 1, 2, 1, out4) == 1    # no waves
+    assert h(64, 0, 1, 1, 1, 3, 1, out4) == 1    # odd tile count
+    assert h(64, 0, 1, 1, 0, 2, 1, out4) == 1    # no workgroups
+    assert h(64, 0, 1, 1, 1, 2, 1, None) == 1    # no output
 
 
 def test_version_and_status_strings(lib):
