@@ -208,12 +208,12 @@ struct ModelShape {
 // staged by direct global-to-LDS loads instead.  D = 64 or 128; W waves per
 // SIMD (256*W threads, one workgroup per CU).  `kv` holds 32 K/V tile pairs
 // per group of eight workgroups that share an XCD, as the 256-query
-// workgroups of one (batch, head) at N = 2048 share them.  Operand values are
-// arbitrary (small fp16 numbers); only the instruction stream, its
-// dependences and the memory traffic follow the forward.  The operand
-// values come from `in` and `kv`: small smooth numbers, or random fp16 values
-// in [-2, 2) like the forward's N(0, 1) inputs (the chip's clock under an
-// MFMA load depends on how many operand bits toggle).
+// workgroups of one (batch, head) at N = 2048 share them.  The instruction
+// stream, its dependences and the memory traffic follow the forward; the
+// values do not (no result is meaningful).  The operands come from `in` and
+// `kv`: small smooth numbers, or random fp16 values in [-2, 2) like the
+// forward's N(0, 1) inputs (the chip's clock under an MFMA load depends on
+// how many operand bits toggle).
 template <int MODE, int D, int W>
 __global__ __launch_bounds__(256 * W) void step_model_probe(const float* __restrict__ in,
                                                            const unsigned char* __restrict__ kv,
