@@ -349,7 +349,7 @@ STEP_MODEL_MODES = ("mfma only", "sequential: S^T, softmax, P V", "pipelined, re
 def step_model_ceiling(torch, d: int, iters: int = 4096, reps: int = 3):
     """TFLOP/s of the step model's full variant (K/V staged through registers,
     two waves per SIMD, random operands) at head dim d, or None when the
-    probe library is not built."""
+    probe library is not built or the probe fails."""
     import ctypes
 
     from exact_attention_fwd_amd import _build
@@ -364,7 +364,9 @@ def step_model_ceiling(torch, d: int, iters: int = 4096, reps: int = 3):
     out = (ctypes.c_double * 4)()
     rc = lib.fa2probe_step_model(d, 6, 2, 1, n_cu * 2, iters, reps, out)
     if rc != 0:
-        raise RuntimeError(f"fa2probe_step_model({d}) failed: {rc}")
+        # context for the bench line, not part of it: report and go on
+        log(f"[bench] fa2probe_step_model({d}) failed ({rc}): no step-model ceiling")
+        return None
     return out[1]
 
 
