@@ -306,20 +306,27 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
     const TrBase vt(lane);
 
     // Keys at or beyond N, and under the causal mask keys after the query,
-    // get -inf.  Accumulator element (kb, r) is key k0 + 32kb + 8(r/4) +
-    // 4hi + r%4.
+    // get -inf.  Accumulator element (kb, r) is key k0 + 4hi + off with
+    // off = 32kb + 8(r/4) + r%4, visible iff off <= lim for this lane's
+    // limit (one compare and one select per element).
     auto mask_tile = [&](int k0, f32x16 (&s)[2]) {
-        const int past_end = k0 + 4 * hi - N;      // key >= N  <=>  past_end + off >= 0
-        const int after_q = k0 + 4 * hi - my_q;    // key > q   <=>  after_q + off > 0
+        int lim = N - 1 - k0 - 4 * hi;                       // key < N
+        if constexpr (CAUSAL) lim = min(lim, my_q - k0 - 4 * hi);   // key <= q
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-                const bool hidden = past_end >= -off || (CAUSAL && after_q > -off);
-                if (hidden) s[kb][r] = -INFINITY;
+                if (off > lim) s[kb][r] = -INFINITY;
             }
         }
+    };
+    // Whether tile t needs mask_tile for this wave: beyond n_full (the
+    // workgroup's bound) it does unless, under the causal mask, every key of
+    // the tile is at or before this wave's first query and inside [0, N)
+    // (wave-uniform).
+    auto needs_mask = [&](int t) {
+        return t >= n_full && (!CAUSAL || (t + 1) * kBK - 1 > qw0 || (t + 1) * kBK > N);
     };
 
     // Prologue.  The V buffer of tile -1 starts zeroed: the first
@@ -385,7 +392,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
         }
     }
     // Reference max from tile 0, so the first iteration needs no correction.
-    if (0 >= n_full) mask_tile(0, s0);
+    if (needs_mask(0)) mask_tile(0, s0);
     {
         float mx = -INFINITY;
 #pragma unroll
@@ -423,7 +430,7 @@ void fa2_fwd_kernel(const _Float16* __restrict__ Q, const _Float16* __restrict__
 #pragma unroll
             for (int db = 0; db < C::kDBlocks; ++db) oacc[db] *= alpha;
         }
-        if (!DEAD && t >= n_full) mask_tile(t * kBK, s_cur);
+        if (!DEAD && needs_mask(t)) mask_tile(t * kBK, s_cur);
 
         // MFMA job p: p < kPV is P V (k-step p / kDBlocks, O^T block
         // p % kDBlocks), then S^T (d-step, key block).  Operands are read
